@@ -1,0 +1,149 @@
+"""Pins for the oracle's scaled GEMM, quantize/amax and padding (CPU only).
+
+* GEMM: brute force with Python integers (every e4m3 value times 2**9 is an
+  integer) on the small-shape configuration, index by index, so a transposed
+  operand, a wrong contraction index or a dropped scale fails;
+* quantize: Q^T is the transpose, padded rows are zero, amax is the brute-force
+  maximum over valid rows and equals |x| of some element;
+* padding: the pages' worked numbers (3858 tokens) and the closed form.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import e4m3, gemm, padding
+from oracle.quantize import amax, bf16_to_f32, quantize_tensorwise
+from oracle.scaling import scale_from_amax
+
+
+def _int_codes(q):
+    """Each code as an exact integer multiple of 2**-9."""
+    return [[int(e4m3.decode_code(c) * 512) for c in row] for row in q]
+
+
+def test_gemm_exact_against_python_integers():
+    d = workloads.linear_inputs(1)
+    x, w = d["x"], d["w"]
+    assert x.shape == (64, 128) and w.shape == (128, 128)
+    sx, sx_inv = scale_from_amax(amax(x))
+    sw, sw_inv = scale_from_amax(amax(w))
+    qx, _, _ = quantize_tensorwise(x, sx_inv)
+    qw, _, _ = quantize_tensorwise(w, sw_inv)
+    A = _int_codes(qx)
+    B = _int_codes(qw)
+    S = gemm.unscaled_product(qx, qw)
+    D = gemm.scaled_gemm(qx, qw, sx, sw)
+    for m in range(64):
+        for n in range(128):
+            acc = 0
+            for k in range(128):
+                acc += A[m][k] * B[n][k]
+            exact = acc / float(1 << 18)          # exact: |acc| < 2**53
+            assert S[m, n] == exact
+            assert D[m, n] == exact * (float(sx) * float(sw))
+
+
+def test_gemm_nonsquare_indices():
+    rng = np.random.default_rng(0)
+    qa = rng.integers(0, 0x7F, size=(3, 5)).astype(np.uint8)   # finite codes only
+    qb = rng.integers(0, 0x7F, size=(2, 5)).astype(np.uint8) | 0x80
+    D = gemm.scaled_gemm(qa, qb, 2.0, 0.5)
+    assert D.shape == (3, 2)
+    for m in range(3):
+        for n in range(2):
+            ref = sum(e4m3.decode_code(qa[m, k]) * e4m3.decode_code(qb[n, k]) for k in range(5))
+            assert D[m, n] == ref
+
+
+def test_gemm_exact_at_large_k():
+    """All-448 operands at K = 2**17 - 16: the float64 sum is still exact."""
+    K = (1 << 17) - 16
+    qa = np.full((1, K), 0x7E, np.uint8)
+    qb = np.full((2, K), 0x7E, np.uint8)
+    qb[1, ::2] = 0x01
+    S = gemm.unscaled_product(qa, qb)
+    assert S[0, 0] == 448 * 448 * K
+    assert S[0, 1] == 448 * 448 * (K // 2) + 448 * 2.0 ** -9 * (K // 2)
+
+
+def test_error_bound_definition():
+    qa = np.array([[0x38, 0x40]], np.uint8)         # [1, 2]
+    qb = np.array([[0x40, 0x38], [0x00, 0x38]], np.uint8)  # [2, 1], [0, 1]
+    b = gemm.error_bound(qa, qb, 1.0, 3.0)
+    assert np.allclose(b, 1e-2 * np.array([[np.sqrt(5) * 3 * np.sqrt(5), np.sqrt(5) * 3]]))
+
+
+def test_quantize_transpose_and_padding():
+    x = workloads.bf16_tensor("normal", (48, 40), 99, 1, 0, std=3.0)
+    x[40:] = 0x7FC0                                  # NaN sentinels in the padded rows
+    q, qt, a = quantize_tensorwise(x, np.float32(10.0), rows_valid=40)
+    assert np.array_equal(qt, q.T)
+    assert np.all(q[40:] == 0)
+    assert not np.isnan(a)
+    vals = [abs(float(v)) for v in bf16_to_f32(x[:40]).ravel()]
+    assert a == np.float32(max(vals))
+    assert a in set(np.abs(bf16_to_f32(x[:40])).ravel())
+
+
+def test_amax_edge_cases():
+    assert amax(np.zeros((4, 4), np.uint16)) == 0.0
+    assert amax(np.full((4, 4), 0x8000, np.uint16)) == 0.0          # -0.0
+    x = np.zeros((4, 4), np.uint16)
+    x[2, 3] = 0xC2F6                                                # -123.0
+    assert amax(x) == 123.0
+    x[1, 1] = 0x7FC0
+    assert np.isnan(amax(x))
+    assert amax(x, rows_valid=1) == 0.0
+    assert amax(np.zeros((0, 8), np.uint16)) == 0.0
+
+
+def test_quantize_uses_float32_product_then_rne():
+    # 1.0625 is the midpoint of 1 and 1.125: ties to even -> 0x38
+    x = np.array([[0x3F88]], np.uint16)                            # bf16 1.0625
+    q, _, _ = quantize_tensorwise(x, np.float32(1.0))
+    assert q[0, 0] == 0x38
+    # bf16 1.0 times the float32 just above 1.0625 -> rounds up to 0x39
+    q, _, _ = quantize_tensorwise(np.array([[0x3F80]], np.uint16),
+                                  np.nextafter(np.float32(1.0625), np.float32(2)))
+    assert q[0, 0] == 0x39
+
+
+def _golden_constants(golden_dir):
+    out = {}
+    with open(os.path.join(golden_dir, "pages_constants.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, value = line.split()[:2]
+            out[name] = value
+    return out
+
+
+def test_padding_worked_numbers(golden_dir):
+    c = _golden_constants(golden_dir)
+    mult = int(c["token_multiple"])
+    bad = int(c["bad_token_count"])
+    assert mult == padding.TOKEN_MULTIPLE == 16
+    assert bad % mult != 0
+    assert padding.pad_amount(bad) == 14 and padding.padded_count(bad) == 3872
+    assert int(c["fp8_weight_bytes"]) == 4096 * 4096 * 1
+    assert int(c["short_storage_bytes"]) == 4092 * 4096
+
+
+@pytest.mark.parametrize("T,mult,pad", [(0, 16, 0), (1, 16, 15), (15, 16, 1), (16, 16, 0),
+                                        (17, 16, 15), (67827, 16, 13), (5, 8, 3), (64, 24, 8)])
+def test_pad_amount(T, mult, pad):
+    assert padding.pad_amount(T, mult) == pad
+    assert padding.padded_count(T, mult) % mult == 0
+    assert 0 <= padding.padded_count(T, mult) - T < mult
+
+
+def test_pad_rows():
+    x = np.arange(3 * 5, dtype=np.uint16).reshape(3, 5) + 1
+    p = padding.pad_rows(x)
+    assert p.shape == (16, 5)
+    assert np.array_equal(p[:3], x) and np.all(p[3:] == 0)
+    with pytest.raises(ValueError):
+        padding.pad_amount(3, 0)
