@@ -27,7 +27,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import e4m3
-from .quantize import bf16_to_f32
+from .quantize import bf16_to_f32, encode_product
 from .scaling import AMAX_FLOOR, E4M3_MAX
 
 BLOCK = 128
@@ -55,8 +55,9 @@ def _quantize_row_tiles(xf: np.ndarray, valid: np.ndarray):
     t = np.abs(np.where(valid, xf, np.float32(0.0))).reshape(R, C // BLOCK, BLOCK)
     tile_amax = np.max(t, axis=2).astype(np.float32)          # NaN propagates
     scale, scale_inv = tile_scales(tile_amax)
-    v = xf * np.repeat(scale_inv, BLOCK, axis=1)               # float32 multiply
-    q = np.where(valid, e4m3.encode(v), np.uint8(0)).astype(np.uint8)
+    with np.errstate(invalid="ignore", over="ignore"):
+        v = xf * np.repeat(scale_inv, BLOCK, axis=1)           # float32 multiply
+    q = np.where(valid, encode_product(xf, v), np.uint8(0)).astype(np.uint8)
     return q, tile_amax, scale
 
 
@@ -87,7 +88,8 @@ def quantize_128x128(w_bits: np.ndarray):
     tile_amax = np.max(t, axis=(1, 3)).astype(np.float32)
     scale, scale_inv = tile_scales(tile_amax)
     full_inv = np.repeat(np.repeat(scale_inv, BLOCK, axis=0), BLOCK, axis=1)
-    q = e4m3.encode(wf * full_inv)
+    with np.errstate(invalid="ignore", over="ignore"):
+        q = encode_product(wf, wf * full_inv)
     return q, np.ascontiguousarray(q.T), tile_amax, scale, np.ascontiguousarray(scale.T)
 
 

@@ -12,6 +12,9 @@ So, for a bf16 tensor X and the float32 multiplier ``scale_inv``:
 
 * ``Q[r, c] = e4m3(float32(X[r, c]) * scale_inv)`` -- one float32 multiply
   (round to nearest even), then the E4M3 encoder of ``oracle.e4m3``;
+* a NaN product (a NaN input, or an invalid multiplier) gives the NaN code
+  0x7F with the SIGN OF THE INPUT x: IEEE 754 does not fix the sign of a NaN
+  that an operation returns, so the input's sign is the one portable choice;
 * ``Q_t`` is the byte-for-byte transpose of ``Q`` (the copy the backward
   GEMMs read; a reading of the hot path, not printed on the pages);
 * ``amax = max |X[r, c]|`` over the valid rows, as float32. bf16 -> float32 is
@@ -44,10 +47,20 @@ def amax(x_bits: np.ndarray, rows_valid: int | None = None) -> np.float32:
     return np.float32(np.max(np.abs(x)))
 
 
+def encode_product(x: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Codes of the float32 products ``v`` of inputs ``x`` (float32, same shape):
+    the E4M3 encoder, except that a NaN product takes the sign of its input."""
+    code = e4m3.encode(v)
+    nan_code = np.where(np.signbit(x), e4m3.NAN_CODE | e4m3.SIGN_BIT, e4m3.NAN_CODE)
+    return np.where(np.isnan(v), nan_code, code).astype(np.uint8)
+
+
 def quantize_values(x_bits: np.ndarray, scale_inv) -> np.ndarray:
     """e4m3 codes of float32(x) * scale_inv, elementwise, any shape."""
-    v = bf16_to_f32(x_bits) * np.float32(scale_inv)   # float32 * float32 -> float32 (RNE)
-    return e4m3.encode(v)
+    x = bf16_to_f32(x_bits)
+    with np.errstate(invalid="ignore", over="ignore"):
+        v = x * np.float32(scale_inv)            # float32 * float32 -> float32 (RNE)
+    return encode_product(x, v)
 
 
 def quantize_tensorwise(x_bits: np.ndarray, scale_inv, rows_valid: int | None = None):

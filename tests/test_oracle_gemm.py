@@ -147,3 +147,14 @@ def test_pad_rows():
     assert np.array_equal(p[:3], x) and np.all(p[3:] == 0)
     with pytest.raises(ValueError):
         padding.pad_amount(3, 0)
+
+
+def test_nan_products_take_the_input_sign():
+    from oracle.quantize import quantize_values
+    x = np.array([0x7FC0, 0xFFC0, 0x7F81, 0xFF81, 0x3F80, 0xBF80, 0x0000, 0x8000], np.uint16)
+    assert list(quantize_values(x, np.float32(2.0))) == [0x7F, 0xFF, 0x7F, 0xFF, 0x40, 0xC0, 0, 0x80]
+    # an invalid multiplier makes every product NaN: the sign still comes from x
+    assert list(quantize_values(x, np.float32(np.nan))) == [0x7F, 0xFF, 0x7F, 0xFF, 0x7F, 0xFF, 0x7F, 0xFF]
+    # inf * 0 is NaN as well
+    z = np.array([0x7F80, 0xFF80], np.uint16)
+    assert list(quantize_values(z, np.float32(0.0))) == [0x7F, 0xFF]
