@@ -1,0 +1,254 @@
+"""Benchmark: fp8 linear fwd+bwd TFLOP/s at 8192x4096x14336, and quantize+amax GB/s.
+
+One step is one pass of the whole hot path over the Llama-8B-shaped MLP block
+(tokens M = 8192; gate and up: K = 4096 -> N = 14336; down: 14336 -> 4096):
+for each of the three linears the weight is quantized (with its amax recorded
+in the 16-entry ring), the input is quantized with its delayed scale, the
+forward GEMM runs, then the gradient is quantized and dgrad and wgrad run, and
+the delayed scales are updated; the token count goes through the padding check
+(8192 is already a multiple of 16, so no rows are added). Inputs are seeded
+synthetic tensors already resident in HBM: activations Student-t(3), weights
+N(0, 0.02), output gradients N(0, 1e-3). Timing: W untimed warm-up steps
+(steady state of delayed scaling), then K steps between two device
+synchronizations; HIP events around every kernel call give per-launch
+durations for the roofline figures.
+
+Prints ONE JSON line. ``--gpus N`` with N > 1 exits: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    return ap.parse_args()
+
+
+class EventProbe:
+    """Records a pair of HIP events (on the current stream) around each tagged kernel call."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+        self.active = False
+        self._tag = None
+
+    def __call__(self, tag):
+        self._tag = tag
+        return self
+
+    def __enter__(self):
+        if self.active:
+            e = self.torch.cuda.Event(enable_timing=True)
+            e.record()
+            self.pairs.setdefault(self._tag, []).append([e, None])
+        return self
+
+    def __exit__(self, *exc):
+        if self.active:
+            e = self.torch.cuda.Event(enable_timing=True)
+            e.record()
+            self.pairs[self._tag][-1][1] = e
+        return False
+
+    def durations_ms(self, tag):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(tag, [])]
+
+
+def cpu_baseline(sample_tokens: int) -> dict:
+    """The CPU oracle, as it is, on a bounded sample of the same workload.
+
+    Sample: the gate linear (K=4096, N=14336) restricted to ``sample_tokens`` tokens
+    (quantize x and g slabs, forward/dgrad/wgrad of the slab in float64) plus the
+    quantize of a 1024-row slab of W; scaled linearly to the full step of three linears
+    (up and down have the same FLOPs and element counts as gate).
+    """
+    import workloads
+    from oracle import gemm
+    from oracle.quantize import quantize_tensorwise
+    from oracle.scaling import scale_from_amax
+    from oracle.quantize import amax as o_amax
+
+    M, K, N = 8192, 4096, 14336
+    S, R = sample_tokens, 1024
+    x = workloads.bf16_tensor("student_t", (S, K), 3, workloads.T_X, 0, nu=3)
+    g = workloads.bf16_tensor("normal", (S, N), 3, workloads.T_GGATE, 0, std=1e-3)
+    w = workloads.bf16_tensor("normal", (R, K), 3, workloads.T_WGATE, 0, std=0.02)
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    _, swi = scale_from_amax(o_amax(w))
+    qw_slab, _, _ = quantize_tensorwise(w, swi)
+    t_w = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    sx, sxi = scale_from_amax(o_amax(x))
+    sg, sgi = scale_from_amax(o_amax(g))
+    qx, qx_t, _ = quantize_tensorwise(x, sxi)
+    qg, qg_t, _ = quantize_tensorwise(g, sgi)
+    t_q = time.perf_counter() - t0
+    # the slab's three GEMMs against a full-size weight (codes tiled from the slab)
+    qw = np.tile(qw_slab, (N // R, 1))
+    qw_t = np.ascontiguousarray(qw.T)
+    t0 = time.perf_counter()
+    gemm.scaled_gemm(qx, qw, sx, 1.0)              # forward  [S, N], contraction K
+    gemm.scaled_gemm(qg, qw_t, sg, 1.0)            # dgrad    [S, K], contraction N
+    gemm.scaled_gemm(qg_t, qx_t, sg, sx)           # wgrad    [N, K], contraction over S tokens
+    t_g = time.perf_counter() - t0
+    t_linear = t_w * (N / R) + (t_q + t_g) * (M / S)
+    t_step = 3 * t_linear
+    flops = 3 * 6.0 * M * N * K
+    return {"value": round(flops / t_step / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"gate linear on {S} of {M} tokens (quantize x,g slabs; fwd, dgrad, wgrad in "
+                       f"float64 via BLAS with {blas_threads} threads) + quantize of {R} of {N} "
+                       f"weight rows (single-threaded numpy), scaled linearly to the 3-linear step; "
+                       f"measured {t_w + t_q + t_g:.1f} s, extrapolated step {t_step:.1f} s")}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build measures one GPU: the hot path runs on one "
+                                   "device and has no cross-GPU step; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import scaled_fp8_linear_amd as m
+    import workloads
+
+    m.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    M, K, N = 8192, 4096, 14336
+
+    host = workloads.mlp_inputs(3)
+
+    def up(b):
+        return torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t = {k: up(v) for k, v in host.items()}
+    del host
+    probe = EventProbe(torch)
+    lins = {n: m.DelayedScalingLinear(dev, probe=probe) for n in ("gate", "up", "down")}
+    shapes = {"gate": (K, N), "up": (K, N), "down": (N, K)}     # (in, out)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    bufs, outs = {}, {}
+    for n, (kin, kout) in shapes.items():
+        bufs[n] = dict(qw=torch.empty((kout, kin), **u8), qw_t=torch.empty((kin, kout), **u8),
+                       qx=torch.empty((M, kin), **u8), qx_t=torch.empty((kin, M), **u8),
+                       qg=torch.empty((M, kout), **u8), qg_t=torch.empty((kout, M), **u8))
+        outs[n] = dict(y=torch.empty((M, kout), **bf), dx=torch.empty((M, kin), **bf),
+                       dw=torch.empty((kout, kin), **bf))
+    inp = {"gate": t["x"], "up": t["x"], "down": t["h"]}
+    wts = {"gate": t["w_gate"], "up": t["w_up"], "down": t["w_down"]}
+    grads = {"gate": t["g_gate"], "up": t["g_up"], "down": t["g_down"]}
+
+    def step():
+        # token-count padding check (8192 is a multiple of 16: nothing to add)
+        _, T_pad = m.fp8_pad_tokens(t["x"], query_only=True)
+        assert T_pad == M
+        for n in ("gate", "up", "down"):
+            lins[n].begin_step()
+        for n in ("gate", "up", "down"):
+            lins[n].forward(inp[n], wts[n], out=outs[n]["y"], bufs=bufs[n])
+        for n in ("down", "up", "gate"):
+            lins[n].backward(grads[n], dx=outs[n]["dx"], dw=outs[n]["dw"], bufs=bufs[n])
+        for n in ("gate", "up", "down"):
+            lins[n].end_step()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    probe.active = True
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    probe.active = False
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    flops_step = 3 * 6.0 * M * N * K
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    gemm_ms = probe.durations_ms("gemm")
+    q_ms = probe.durations_ms("quantize")
+    s_ms = probe.durations_ms("scale")
+    gemm_avg = float(np.mean(gemm_ms))
+    gemm_flops = 2.0 * M * N * K                   # every one of the 9 GEMMs has this count
+    gemm_tflops = gemm_flops / (gemm_avg * 1e-3) / 1e12
+    q_elems_step = 3 * (M * K + N * K + M * N)     # per linear: x, W, g (equal across the three)
+    q_bytes_step = 4 * q_elems_step                # 2 B read + 1 B Q + 1 B Q^T per element
+    q_ms_step = float(np.sum(q_ms)) / args.steps
+    q_gbs = q_bytes_step / (q_ms_step * 1e-3) / 1e9
+    line = {
+        "metric": "fp8 linear fwd+bwd TFLOP/s at 8192x4096x14336; quantize+amax GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "Llama-8B-shaped MLP block fwd+bwd (gate, up: 4096->14336; "
+                               "down: 14336->4096), delayed tensorwise scaling",
+                   "tokens": M, "K": K, "N": N, "linears": 3, "flops_per_step": flops_step},
+        "roofline": {"bound": "mfma", "kernel": "gemm_fp8_kernel",
+                     "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "avg_launch_us": round(gemm_avg * 1e3, 2),
+                     "launches": len(gemm_ms)},
+        "quantize_amax": {"achieved": round(q_gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                          "frac": round(q_gbs / PEAK_HBM_GBS, 4),
+                          "avg_launch_us": round(float(np.mean(q_ms)) * 1e3, 2),
+                          "bytes_per_step": q_bytes_step},
+        "breakdown_ms_per_step": {"gemm": round(float(np.sum(gemm_ms)) / args.steps, 4),
+                                  "quantize": round(q_ms_step, 4),
+                                  "scale_update": round(float(np.sum(s_ms)) / args.steps, 4)},
+        "gemm_only_tflops": round(9 * gemm_flops / (float(np.sum(gemm_ms)) / args.steps * 1e-3)
+                                  / 1e12, 2),
+        "wall_s_timed": round(wall_s, 3),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+/*
+ * fp8lin.h -- C ABI of the MI355X (gfx950) scaled FP8 linear layer.
+ *
+ * The layer is y = x W^T computed as a "TE-style" scaled FP8 linear:
+ * operands are quantized to OCP e4m3 with per-tensor (or per-tile) float32
+ * scales, multiplied on the FP8 matrix cores with float32 accumulation, and
+ * the scales are folded in after accumulation. Sources, cited per function:
+ *
+ *   [AstrAI]    AstrAI, astrai/extension/fp8_state.py (module comment on the
+ *               GEMM layout, FP8TensorMeta, FP8State.step,
+ *               _update_delayed_scale, fp8_linear_forward/backward).
+ *   [SpecForge] SpecForge PR 2, "Add training.fp8_linear: torchao
+ *               Float8Linear with float8 all-gather", Conclusion
+ *               (Constraints bullet) and Modifications.
+ *   [NeMo]      NeMo PR 15754, "Add FP8 support for SALMAutomodel", review
+ *               thread on BSHD/THD padding; TE's "recipe=block".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is DEVICE memory on the current HIP device, owned
+ *   and allocated by the caller; the library allocates nothing and keeps no
+ *   state between calls (it is safe to call from several host threads).
+ * - Layouts are dense row-major. bf16 tensors are 2 bytes per element, e4m3
+ *   tensors 1 byte per element (OCP E4M3: bias 7, max 448, NaN 0x7F/0xFF,
+ *   no infinities), scales and amaxes are float32.
+ * - `stream` is a hipStream_t passed as void*; NULL is the null stream. All
+ *   work is enqueued asynchronously on it; nothing synchronizes the host.
+ * - Return value: FP8_OK, or an fp8_status error code for arguments rejected
+ *   on the host before anything is enqueued (then fp8_last_error() says
+ *   why), or FP8_ERR_HIP if a launch failed. Faults inside kernels surface
+ *   at the caller's next synchronization, as usual for HIP.
+ * - Pointers must be 16-byte aligned; row counts / column counts must be
+ *   multiples of 16 where stated ([SpecForge]: FP8 GEMMs need the token count
+ *   and every converted dimension divisible by 16).
+ * - Sizes are int64_t; every operand of a GEMM must hold fewer than 2^31
+ *   bytes, and the contraction length must be below 2^17.
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8_status {
+  FP8_OK = 0,
+  FP8_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  FP8_ERR_SHAPE = 2,       /* a size is negative, not a multiple of 16, ... */
+  FP8_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned              */
+  FP8_ERR_UNSUPPORTED = 4, /* valid request this build does not implement   */
+  FP8_ERR_HIP = 5          /* a HIP launch or runtime call failed           */
+} fp8_status;
+
+/* Scaling granularity of a quantized operand. */
+typedef enum fp8_granularity {
+  FP8_TENSORWISE = 0,   /* one float32 scale per tensor                        */
+  FP8_BLOCK_1x128 = 1,  /* one scale per 1x128 tile along the contraction dim  */
+  FP8_BLOCK_128x128 = 2 /* one scale per 128x128 tile (weights)                */
+} fp8_granularity;
+
+/* Modes of fp8_scale_update. */
+typedef enum fp8_scale_mode {
+  FP8_SCALE_FROM_AMAX = 0, /* scale, scale_inv from one amax (delayed or current) */
+  FP8_SCALE_RECORD = 1,    /* push an amax into the weight history ring           */
+  FP8_SCALE_REFRESH = 2    /* scale, scale_inv from the maximum of the ring       */
+} fp8_scale_mode;
+
+/*
+ * fp8_quantize_amax -- fused bf16 -> e4m3 quantize with its amax, emitting
+ * the row-major codes and their transpose in one pass over x.
+ *
+ * Source: [AstrAI] module comment ("D = A_SCALE * B_SCALE * A * B", scales
+ * amax/448, quantization multiplies by 1/scale) and fp8_linear_forward's
+ * docstring (the quantize kernel emits the current amax; no separate
+ * abs/max reduce).
+ *
+ *   x          bf16 [rows, cols], read-only.
+ *   rows, cols >= 0, both multiples of 16 (multiples of 128 in BLOCK modes).
+ *   rows_valid 0 <= rows_valid <= rows. Rows r >= rows_valid are token
+ *              padding: they are NOT read (they may hold anything), they do
+ *              not enter amax, and their codes are written as 0x00.
+ *   gran       FP8_TENSORWISE, FP8_BLOCK_1x128 or FP8_BLOCK_128x128.
+ *
+ * FP8_TENSORWISE:
+ *   scale_inv  float32 [1]: the multiplier 448/amax of the scale in force.
+ *              Required when q or q_t is non-NULL.
+ *   q          e4m3 [rows, cols] or NULL:  q[r,c] = e4m3(float32(x[r,c]) * *scale_inv),
+ *              one float32 multiply rounded to nearest even, then round to
+ *              nearest even on the e4m3 grid, saturating to +-448; NaN stays
+ *              NaN (0x7F with its sign); -0 and negative underflow give 0x80.
+ *   q_t        e4m3 [cols, rows] or NULL: q_t[c,r] = q[r,c].
+ *   amax       float32 [1] or NULL: OVERWRITTEN with max |x[r,c]| over the
+ *              valid rows (exact; 0 for empty input; NaN if a valid element is
+ *              NaN). Computed on the same pass.
+ *   scale, scale_t  must be NULL.
+ *
+ * FP8_BLOCK_1x128 (activations, gradients; current per-tile scaling):
+ *   scale_inv  must be NULL (each tile's multiplier is computed in the pass
+ *              as 448/max(tile_amax, 1e-12) with IEEE division).
+ *   q, scale   q e4m3 [rows, cols] with tiles of 1x128 along cols;
+ *              scale float32 [rows, cols/128] = max(tile_amax,1e-12)/448.
+ *              Both NULL or both non-NULL.
+ *   q_t, scale_t  the transposed copy QUANTIZED AGAIN with 1x128 tiles along
+ *              rows (the contraction index of wgrad): q_t e4m3 [cols, rows],
+ *              scale_t float32 [cols, rows/128]. Both NULL or both non-NULL.
+ *   amax       float32 [rows, cols/128] or NULL: the tile amaxes of q's tiles.
+ *
+ * FP8_BLOCK_128x128 (weights): rows_valid must equal rows.
+ *   q, scale   scale float32 [rows/128, cols/128].
+ *   q_t, scale_t  q_t[c,r] = q[r,c]; scale_t [cols/128, rows/128] is the
+ *              transposed grid (the same tiles).
+ *   amax       float32 [rows/128, cols/128] or NULL.
+ *
+ * Errors: FP8_ERR_NULL (x NULL with rows*cols > 0, required output missing),
+ * FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_HIP.
+ */
+int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_valid,
+                      int gran, const float* scale_inv, void* q, void* q_t, float* amax,
+                      float* scale, float* scale_t, void* stream);
+
+/*
+ * fp8_scale_update -- the delayed-scaling bookkeeping, on the device.
+ *
+ * Source: [AstrAI] _update_delayed_scale, FP8TensorMeta.record/refresh,
+ * FP8State.step.
+ *
+ * FP8_SCALE_FROM_AMAX: a = max(amax[0], 1e-12f) (NaN is kept);
+ *   scale[0] = a / 448, scale_inv[0] = 448 / a, each ONE correctly rounded
+ *   float32 division. Called after the pass that produced amax, this is the
+ *   one-step-delayed activation/gradient update; called before the
+ *   quantize pass on the same tensor it is current scaling. hist, len, pos
+ *   are ignored.
+ * FP8_SCALE_RECORD: hist[pos] = amax[0]; 0 <= pos < len. The ring index
+ *   lives on the host ([AstrAI] record keeps idx as a Python int), so the
+ *   caller advances pos = (pos + 1) % len. scale, scale_inv are ignored.
+ * FP8_SCALE_REFRESH: m = max(hist[0..len)) (NaN propagates); if m > 0:
+ *   scale[0] = m / 448, scale_inv[0] = 448 / m; otherwise both are left as
+ *   they were. amax and pos are ignored. The ring starts as all ones and the
+ *   caller refreshes when its step counter reaches a multiple of 16.
+ *
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE (len < 1, pos out of range, bad mode
+ * -> FP8_ERR_UNSUPPORTED), FP8_ERR_HIP.
+ */
+int fp8_scale_update(int mode, const float* amax, float* hist, int32_t len, int32_t pos,
+                     float* scale, float* scale_inv, void* stream);
+
+/*
+ * fp8_linear_fwd -- y = x W^T as the scaled FP8 GEMM.
+ *
+ * Source: [AstrAI] module comment "D = A_SCALE * B_SCALE * A * B" and
+ * fp8_linear_forward (the scaled forward kernel call).
+ *
+ *   qx  e4m3 [M, K], qw e4m3 [N, K] (both contraction-index-last).
+ *   y   bf16 [M, N]: y[m,n] = bf16_rne(sx * sw * sum_k qx[m,k] * qw[n,k])
+ *       for m < M_valid (float32 accumulation on the matrix cores, scales
+ *       applied in float32 after accumulation), y[m,n] = 0 for m >= M_valid.
+ *   FP8_TENSORWISE: sx, sw float32 [1] (dequant scales amax/448).
+ *   FP8_BLOCK_1x128 (the block recipe): sx [M, K/128], sw [N/128, K/128];
+ *       the scales multiply each 128-wide partial sum.
+ *   M, N, K multiples of 16 (K, N multiples of 128 in the block recipe);
+ *   0 <= M_valid <= M.
+ */
+int fp8_linear_fwd(const void* qx, const void* qw, const float* sx, const float* sw, void* y,
+                   int64_t M, int64_t N, int64_t K, int64_t M_valid, int gran, void* stream);
+
+/*
+ * fp8_linear_dgrad -- dx = g W from the e4m3 gradient and W's transposed copy.
+ *
+ * Source: [AstrAI] fp8_linear_backward (input gradient of the scaled backward).
+ *
+ *   qg  e4m3 [M, N], qw_t e4m3 [K, N] (the q_t output of quantizing W [N, K]).
+ *   dx  bf16 [M, K]: dx[m,k] = bf16_rne(sg * sw * sum_n qg[m,n] * qw_t[k,n])
+ *       for m < M_valid, 0 otherwise.
+ *   FP8_TENSORWISE: sg, sw float32 [1].
+ *   FP8_BLOCK_1x128: sg [M, N/128], sw = W's scale_t grid [K/128, N/128].
+ */
+int fp8_linear_dgrad(const void* qg, const void* qw_t, const float* sg, const float* sw, void* dx,
+                     int64_t M, int64_t N, int64_t K, int64_t M_valid, int gran, void* stream);
+
+/*
+ * fp8_linear_wgrad -- dW = g^T x from the two transposed copies.
+ *
+ * Source: [AstrAI] fp8_linear_backward (weight gradient); [SpecForge]
+ * Constraints bullet: this GEMM contracts over the token count M, which is
+ * why M must be a multiple of 16.
+ *
+ *   qg_t e4m3 [N, M], qx_t e4m3 [K, M] (q_t outputs of quantizing g and x).
+ *   dw   bf16 [N, K]: dw[n,k] = bf16_rne(sg * sx * sum_m qg_t[n,m] * qx_t[k,m]).
+ *        Padded tokens contribute nothing because their codes are 0x00.
+ *   FP8_TENSORWISE: sg, sx float32 [1] -- sx must be the scale that
+ *        quantized x in the forward (not the updated one).
+ *   FP8_BLOCK_1x128: sg = g's scale_t [N, M/128], sx = x's scale_t [K, M/128].
+ */
+int fp8_linear_wgrad(const void* qg_t, const void* qx_t, const float* sg, const float* sx, void* dw,
+                     int64_t M, int64_t N, int64_t K, int gran, void* stream);
+
+/*
+ * fp8_pad_tokens -- pad a packed token batch to a multiple of `multiple` rows.
+ *
+ * Source: [NeMo] review thread, "pad = (-T) % seq_multiple"; [SpecForge]
+ * Constraints bullet (multiple of 16 for float8 GEMMs).
+ *
+ *   x        bf16 [T, cols] (read-only unless x_pad == x).
+ *   T, cols  >= 0; multiple >= 1.
+ *   T_pad    host int64 out: T + ((-T) mod multiple). Required.
+ *   x_pad    NULL: only T_pad is computed (nothing is enqueued).
+ *            == x: in place; the buffer holds T_pad rows and rows [T, T_pad)
+ *            are zeroed.
+ *            otherwise bf16 [T_pad, cols]: rows [0, T) copied, [T, T_pad) zeroed.
+ *   Padding goes at the end of the concatenated batch.
+ */
+int fp8_pad_tokens(const void* x, int64_t T, int64_t cols, int32_t multiple, void* x_pad,
+                   int64_t* T_pad, void* stream);
+
+/* Message for the last error returned on the calling thread ("" if none). */
+const char* fp8_last_error(void);
+
+/* Library version, e.g. "fp8lin 0.1 gfx950". */
+const char* fp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LIN_H */

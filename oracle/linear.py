@@ -55,8 +55,7 @@ class DelayedLinear:
         qx, qx_t, amax_x = quantize_tensorwise(x_bits, sx_inv, rv)
         y = scaled_gemm(qx, qw, sx, sw)
         y[rv:] = 0.0
-        self.w.record(amax_w)
-        self.x_scale, self.x_scale_inv = scale_from_amax(amax_x)
+        self._finish_forward(amax_w, amax_x)
         self._saved = dict(qw_t=qw_t, qx_t=qx_t, sx=sx, sw=sw, rv=rv)
         return dict(y=y, qx=qx, qx_t=qx_t, qw=qw, qw_t=qw_t, amax_x=amax_x,
                     amax_w=amax_w, sx=sx, sx_inv=sx_inv, sw=sw, sw_inv=sw_inv)
@@ -69,8 +68,29 @@ class DelayedLinear:
         dx = scaled_gemm(qg, s["qw_t"], sg, s["sw"])
         dx[rv:] = 0.0
         dw = scaled_gemm(qg_t, s["qx_t"], sg, s["sx"])
-        self.g_scale, self.g_scale_inv = scale_from_amax(amax_g)
+        self._finish_backward(amax_g)
         return dict(dx=dx, dw=dw, qg=qg, qg_t=qg_t, amax_g=amax_g, sg=sg, sg_inv=sg_inv)
+
+    def _finish_forward(self, amax_w, amax_x) -> None:
+        """After the forward: record the weight amax, delay the activation scale."""
+        self.w.record(amax_w)
+        self.x_scale, self.x_scale_inv = scale_from_amax(amax_x)
+
+    def _finish_backward(self, amax_g) -> None:
+        """After the backward: delay the gradient scale."""
+        self.g_scale, self.g_scale_inv = scale_from_amax(amax_g)
+
+    def scales_only_step(self, x_bits, w_bits, g_bits, rows_valid=None) -> dict:
+        """The same bookkeeping as forward + backward without the GEMMs (for long runs at
+        full size). Returns the scales in force during this step and the three amaxes."""
+        rv = x_bits.shape[0] if rows_valid is None else int(rows_valid)
+        used = dict(sw=self.w.scale, sw_inv=self.w.scale_inv, sx=self.x_scale,
+                    sx_inv=self.x_scale_inv, sg=self.g_scale, sg_inv=self.g_scale_inv)
+        aw, ax, ag = amax_of(w_bits), amax_of(x_bits, rv), amax_of(g_bits, rv)
+        self._finish_forward(aw, ax)
+        self._finish_backward(ag)
+        used.update(amax_w=aw, amax_x=ax, amax_g=ag)
+        return used
 
     def state(self) -> dict:
         return dict(step=self.counter.step_count, w_scale=self.w.scale,

@@ -1,0 +1,18 @@
+"""MI355X (gfx950) scaled FP8 linear layer.
+
+The compute path is ``libfp8lin.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/fp8lin.h``); this package is its thin Python binding
+(``_abi``) plus the host-side delayed-scaling schedule (``state``). PyTorch is
+used for device memory and streams only. Importing works without the built
+library; calling any entry point without it raises.
+"""
+from ._abi import (FP8_BLOCK_1x128, FP8_BLOCK_128x128, FP8_SCALE_FROM_AMAX, FP8_SCALE_RECORD,
+                   FP8_SCALE_REFRESH, FP8_TENSORWISE, Fp8Error, Slot, fp8_last_error,
+                   fp8_linear_dgrad, fp8_linear_fwd, fp8_linear_wgrad, fp8_pad_tokens,
+                   fp8_quantize_amax, fp8_scale_update, fp8_version, load)
+from .state import DelayedScalingLinear
+
+__all__ = ["fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
+           "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version", "load",
+           "Fp8Error", "Slot", "DelayedScalingLinear", "FP8_TENSORWISE", "FP8_BLOCK_1x128",
+           "FP8_BLOCK_128x128", "FP8_SCALE_FROM_AMAX", "FP8_SCALE_RECORD", "FP8_SCALE_REFRESH"]

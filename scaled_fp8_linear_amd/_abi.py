@@ -1,0 +1,252 @@
+"""ctypes binding of ``libfp8lin.so``: argument marshalling only.
+
+Each function here has the name of the C entry point it calls and passes
+device pointers, sizes and the current HIP stream through. Every step of the
+computation runs in the library's kernels; PyTorch only provides device
+memory (outputs the caller did not pass are allocated with ``torch.empty``)
+and the stream. If the library is missing this module raises: there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8lin.so")
+
+FP8_OK, FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = range(6)
+FP8_TENSORWISE, FP8_BLOCK_1x128, FP8_BLOCK_128x128 = 0, 1, 2
+FP8_SCALE_FROM_AMAX, FP8_SCALE_RECORD, FP8_SCALE_REFRESH = 0, 1, 2
+
+EXPORTS = ("fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
+           "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version")
+
+
+class Fp8Error(RuntimeError):
+    """An fp8lin entry point returned an error status."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed (status {status}): {msg}")
+        self.status = status
+
+
+_lib = None
+
+_i64, _i32, _int, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_void_p
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once; raise if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m scaled_fp8_linear_amd.build` "
+                           "(the HIP library is required; there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    lib.fp8_quantize_amax.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.fp8_scale_update.argtypes = [_int, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
+    lib.fp8_linear_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
+    lib.fp8_linear_dgrad.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
+    lib.fp8_linear_wgrad.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]
+    lib.fp8_pad_tokens.argtypes = [_vp, _i64, _i64, _i32, _vp, ctypes.POINTER(_i64), _vp]
+    for name in EXPORTS[:6]:
+        getattr(lib, name).restype = _int
+    lib.fp8_last_error.restype = ctypes.c_char_p
+    lib.fp8_last_error.argtypes = []
+    lib.fp8_version.restype = ctypes.c_char_p
+    lib.fp8_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != FP8_OK:
+        raise Fp8Error(fn, status, load().fp8_last_error().decode())
+
+
+def _ptr(t, offset_elems: int = 0):
+    """Device address of a tensor (plus an element offset), or None."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("fp8lin takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("fp8lin takes contiguous row-major tensors")
+    return t.data_ptr() + offset_elems * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _codes(t):
+    """uint8 view of an e4m3 code tensor (uint8 or float8_e4m3fn storage)."""
+    if t is None:
+        return None
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise ValueError(f"e4m3 codes must be uint8 or float8_e4m3fn, got {t.dtype}")
+    return t
+
+
+def _bf16(t):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError(f"expected a bf16 tensor, got {t.dtype}")
+    return t
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    return t
+
+
+class Slot:
+    """A float32 element inside a device tensor (a scale slot), passed by address."""
+
+    def __init__(self, tensor, index: int = 0):
+        _f32(tensor, "slot")
+        self.tensor, self.index = tensor, int(index)
+
+    def ptr(self):
+        return _ptr(self.tensor, self.index)
+
+
+def _fptr(v, name):
+    if v is None:
+        return None
+    if isinstance(v, Slot):
+        return v.ptr()
+    return _ptr(_f32(v, name))
+
+
+def fp8_quantize_amax(x, rows_valid=None, gran=FP8_TENSORWISE, scale_inv=None, q=None, q_t=None,
+                      amax=None, scale=None, scale_t=None, want_q=True, want_q_t=True,
+                      want_amax=True, stream=None):
+    """Quantize a bf16 [rows, cols] tensor. Returns (q, q_t, amax, scale, scale_t).
+
+    Outputs that are not passed in are allocated here (``want_*`` False skips them).
+    """
+    _bf16(x)
+    rows, cols = x.shape
+    rv = rows if rows_valid is None else int(rows_valid)
+    dev = x.device
+    if want_q and q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if want_q_t and q_t is None:
+        q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if gran == FP8_TENSORWISE:
+        if want_amax and amax is None:
+            amax = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        grid_r = rows // 128
+        if want_amax and amax is None:
+            amax = torch.empty((rows if gran == FP8_BLOCK_1x128 else grid_r, cols // 128),
+                               dtype=torch.float32, device=dev)
+        if q is not None and scale is None:
+            scale = torch.empty((rows if gran == FP8_BLOCK_1x128 else grid_r, cols // 128),
+                                dtype=torch.float32, device=dev)
+        if q_t is not None and scale_t is None:
+            scale_t = torch.empty((cols if gran == FP8_BLOCK_1x128 else cols // 128, grid_r),
+                                  dtype=torch.float32, device=dev)
+    q, q_t = _codes(q), _codes(q_t)
+    _check("fp8_quantize_amax", load().fp8_quantize_amax(
+        _ptr(x), rows, cols, rv, gran, _fptr(scale_inv, "scale_inv"), _ptr(q), _ptr(q_t),
+        _fptr(amax, "amax"), _fptr(scale, "scale"), _fptr(scale_t, "scale_t"), _stream(stream)))
+    return q, q_t, amax, scale, scale_t
+
+
+def fp8_scale_update(mode, amax=None, hist=None, pos=0, scale=None, scale_inv=None, stream=None):
+    """One scale bookkeeping op on the device (see fp8lin.h for the modes)."""
+    length = 0 if hist is None else hist.numel()
+    _check("fp8_scale_update", load().fp8_scale_update(
+        int(mode), _fptr(amax, "amax"), _fptr(hist, "hist"), length, int(pos),
+        _fptr(scale, "scale"), _fptr(scale_inv, "scale_inv"), _stream(stream)))
+
+
+def fp8_linear_fwd(qx, qw, sx, sw, y=None, M_valid=None, gran=FP8_TENSORWISE, stream=None):
+    """y [M, N] bf16 = sx * sw * qx [M, K] . qw [N, K]^T."""
+    qx, qw = _codes(qx), _codes(qw)
+    M, K = qx.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("qx and qw contraction sizes differ")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
+    mv = M if M_valid is None else int(M_valid)
+    _check("fp8_linear_fwd", load().fp8_linear_fwd(
+        _ptr(qx), _ptr(qw), _fptr(sx, "sx"), _fptr(sw, "sw"), _ptr(y), M, N, K, mv, gran,
+        _stream(stream)))
+    return y
+
+
+def fp8_linear_dgrad(qg, qw_t, sg, sw, dx=None, M_valid=None, gran=FP8_TENSORWISE, stream=None):
+    """dx [M, K] bf16 = sg * sw * qg [M, N] . qw_t [K, N]^T."""
+    qg, qw_t = _codes(qg), _codes(qw_t)
+    M, N = qg.shape
+    K = qw_t.shape[0]
+    if qw_t.shape[1] != N:
+        raise ValueError("qg and qw_t contraction sizes differ")
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=qg.device)
+    mv = M if M_valid is None else int(M_valid)
+    _check("fp8_linear_dgrad", load().fp8_linear_dgrad(
+        _ptr(qg), _ptr(qw_t), _fptr(sg, "sg"), _fptr(sw, "sw"), _ptr(dx), M, N, K, mv, gran,
+        _stream(stream)))
+    return dx
+
+
+def fp8_linear_wgrad(qg_t, qx_t, sg, sx, dw=None, gran=FP8_TENSORWISE, stream=None):
+    """dw [N, K] bf16 = sg * sx * qg_t [N, M] . qx_t [K, M]^T."""
+    qg_t, qx_t = _codes(qg_t), _codes(qx_t)
+    N, M = qg_t.shape
+    K = qx_t.shape[0]
+    if qx_t.shape[1] != M:
+        raise ValueError("qg_t and qx_t contraction sizes differ")
+    if dw is None:
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=qg_t.device)
+    _check("fp8_linear_wgrad", load().fp8_linear_wgrad(
+        _ptr(qg_t), _ptr(qx_t), _fptr(sg, "sg"), _fptr(sx, "sx"), _ptr(dw), M, N, K, gran,
+        _stream(stream)))
+    return dw
+
+
+def fp8_pad_tokens(x, T=None, multiple=16, x_pad=None, query_only=False, stream=None):
+    """Pad a bf16 [T, cols] batch to a multiple of ``multiple`` rows.
+
+    Returns ``(x_pad, T_pad)``. With ``query_only`` only T_pad is computed. If
+    ``x_pad is x`` the tail of x's own buffer (which must hold T_pad rows) is
+    zeroed in place, with T given explicitly.
+    """
+    cols = x.shape[1]
+    T = x.shape[0] if T is None else int(T)
+    out = ctypes.c_int64(0)
+    lib = load()
+    if query_only:
+        _check("fp8_pad_tokens", lib.fp8_pad_tokens(None, T, cols, int(multiple), None,
+                                                    ctypes.byref(out), None))
+        return None, out.value
+    _check("fp8_pad_tokens", lib.fp8_pad_tokens(None, T, cols, int(multiple), None,
+                                                ctypes.byref(out), None))
+    T_pad = out.value
+    if x_pad is None:
+        x_pad = torch.empty((T_pad, cols), dtype=x.dtype, device=x.device)
+    if x_pad.shape[0] < T_pad:
+        raise ValueError(f"x_pad holds {x_pad.shape[0]} rows, needs {T_pad}")
+    _check("fp8_pad_tokens", lib.fp8_pad_tokens(_ptr(_bf16(x)), T, cols, int(multiple),
+                                                _ptr(x_pad), ctypes.byref(out), _stream(stream)))
+    return x_pad, T_pad
+
+
+def fp8_last_error() -> str:
+    return load().fp8_last_error().decode()
+
+
+def fp8_version() -> str:
+    return load().fp8_version().decode()

@@ -1,0 +1,207 @@
+// C ABI of the scaled FP8 linear layer: argument checking and dispatch.
+// The declarations, with the meaning of every argument, are in include/fp8lin.h.
+#include "../../include/fp8lin.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FP8_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
+constexpr int64_t kMaxContraction = (int64_t)1 << 17;
+
+// Checks shared by the three GEMM entry points. A is [rows_a, kc], B is [rows_b, kc].
+int check_gemm(const char* fn, const void* a, const void* b, const float* s1, const float* s2,
+               const void* d, int64_t rows_a, int64_t rows_b, int64_t kc, int64_t m_valid,
+               int gran) {
+  if (rows_a < 0 || rows_b < 0 || kc < 0)
+    return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
+  if (rows_a % 16 || rows_b % 16 || kc % 16)
+    return fail(FP8_ERR_SHAPE,
+                "%s: sizes must be multiples of 16 (got %lld x %lld x %lld); FP8 GEMMs need the "
+                "token count and every dimension divisible by 16",
+                fn, (long long)rows_a, (long long)rows_b, (long long)kc);
+  if (m_valid < 0 || m_valid > rows_a)
+    return fail(FP8_ERR_SHAPE, "%s: M_valid=%lld outside [0, %lld]", fn, (long long)m_valid,
+                (long long)rows_a);
+  if (gran != FP8_TENSORWISE && gran != FP8_BLOCK_1x128)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: granularity %d (use FP8_TENSORWISE or FP8_BLOCK_1x128)",
+                fn, gran);
+  if (gran == FP8_BLOCK_1x128 && kc % 128)
+    return fail(FP8_ERR_SHAPE, "%s: block recipe needs the contraction size %% 128 == 0 (got %lld)",
+                fn, (long long)kc);
+  if (rows_a * kc >= kMaxOperandBytes || rows_b * kc >= kMaxOperandBytes)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: an operand holds 2^31 bytes or more", fn);
+  if (kc >= kMaxContraction)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: contraction size %lld >= 2^17", fn, (long long)kc);
+  if (rows_a * rows_b > 0) {
+    if (!d || !s1 || !s2) return fail(FP8_ERR_NULL, "%s: NULL output or scale pointer", fn);
+    if (kc > 0 && (!a || !b)) return fail(FP8_ERR_NULL, "%s: NULL operand", fn);
+    if (!aligned16(a) || !aligned16(b) || !aligned16(d))
+      return fail(FP8_ERR_ALIGN, "%s: operands and output must be 16-byte aligned", fn);
+  }
+  return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_last_error(void) { return g_err; }
+
+const char* fp8_version(void) { return "fp8lin 0.1 gfx950"; }
+
+int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_valid, int gran,
+                      const float* scale_inv, void* q, void* q_t, float* amax, float* scale,
+                      float* scale_t, void* stream) {
+  const char* fn = "fp8_quantize_amax";
+  if (rows < 0 || cols < 0) return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
+  if (rows_valid < 0 || rows_valid > rows)
+    return fail(FP8_ERR_SHAPE, "%s: rows_valid=%lld outside [0, %lld]", fn, (long long)rows_valid,
+                (long long)rows);
+  const int64_t mult = (gran == FP8_TENSORWISE) ? 16 : 128;
+  if (rows % mult || cols % mult)
+    return fail(FP8_ERR_SHAPE, "%s: rows and cols must be multiples of %lld (got %lld x %lld)", fn,
+                (long long)mult, (long long)rows, (long long)cols);
+  if (rows * cols > 0 && !x) return fail(FP8_ERR_NULL, "%s: x is NULL", fn);
+  if (!aligned16(x) || !aligned16(q) || !aligned16(q_t))
+    return fail(FP8_ERR_ALIGN, "%s: x, q and q_t must be 16-byte aligned", fn);
+  const hipStream_t s = as_stream(stream);
+  auto* xb = static_cast<const uint16_t*>(x);
+  auto* qb = static_cast<uint8_t*>(q);
+  auto* qtb = static_cast<uint8_t*>(q_t);
+  switch (gran) {
+    case FP8_TENSORWISE:
+      if ((q || q_t) && !scale_inv) return fail(FP8_ERR_NULL, "%s: scale_inv is NULL", fn);
+      if (scale || scale_t)
+        return fail(FP8_ERR_UNSUPPORTED, "%s: scale/scale_t are outputs of the block modes only", fn);
+      return hip_status(
+          fp8lin::launch_quantize_tensorwise(xb, rows, cols, rows_valid, scale_inv, qb, qtb, amax, s),
+          fn);
+    case FP8_BLOCK_1x128:
+    case FP8_BLOCK_128x128:
+      if (scale_inv)
+        return fail(FP8_ERR_UNSUPPORTED, "%s: block modes compute their own multipliers; pass NULL", fn);
+      if ((q == nullptr) != (scale == nullptr))
+        return fail(FP8_ERR_NULL, "%s: q and scale must both be given or both be NULL", fn);
+      if ((q_t == nullptr) != (scale_t == nullptr))
+        return fail(FP8_ERR_NULL, "%s: q_t and scale_t must both be given or both be NULL", fn);
+      if (gran == FP8_BLOCK_128x128) {
+        if (rows_valid != rows)
+          return fail(FP8_ERR_SHAPE, "%s: 128x128 tiles (weights) take no padding rows", fn);
+        return hip_status(fp8lin::launch_quantize_block_128x128(xb, rows, cols, qb, qtb, amax,
+                                                                scale, scale_t, s),
+                          fn);
+      }
+      return hip_status(fp8lin::launch_quantize_block_1x128(xb, rows, cols, rows_valid, qb, qtb,
+                                                            amax, scale, scale_t, s),
+                        fn);
+    default:
+      return fail(FP8_ERR_UNSUPPORTED, "%s: unknown granularity %d", fn, gran);
+  }
+}
+
+int fp8_scale_update(int mode, const float* amax, float* hist, int32_t len, int32_t pos,
+                     float* scale, float* scale_inv, void* stream) {
+  const char* fn = "fp8_scale_update";
+  switch (mode) {
+    case FP8_SCALE_FROM_AMAX:
+      if (!amax || !scale || !scale_inv) return fail(FP8_ERR_NULL, "%s: NULL pointer", fn);
+      break;
+    case FP8_SCALE_RECORD:
+      if (!amax || !hist) return fail(FP8_ERR_NULL, "%s: NULL pointer", fn);
+      if (len < 1 || pos < 0 || pos >= len)
+        return fail(FP8_ERR_SHAPE, "%s: pos=%d outside a ring of %d", fn, pos, len);
+      break;
+    case FP8_SCALE_REFRESH:
+      if (!hist || !scale || !scale_inv) return fail(FP8_ERR_NULL, "%s: NULL pointer", fn);
+      if (len < 1) return fail(FP8_ERR_SHAPE, "%s: empty history", fn);
+      break;
+    default:
+      return fail(FP8_ERR_UNSUPPORTED, "%s: unknown mode %d", fn, mode);
+  }
+  return hip_status(fp8lin::launch_scale_update(mode, amax, hist, len, pos, scale, scale_inv,
+                                                as_stream(stream)),
+                    fn);
+}
+
+int fp8_linear_fwd(const void* qx, const void* qw, const float* sx, const float* sw, void* y,
+                   int64_t M, int64_t N, int64_t K, int64_t M_valid, int gran, void* stream) {
+  int e = check_gemm("fp8_linear_fwd", qx, qw, sx, sw, y, M, N, K, M_valid, gran);
+  if (e) return e;
+  if (gran == FP8_BLOCK_1x128 && N % 128)
+    return fail(FP8_ERR_SHAPE, "fp8_linear_fwd: block recipe needs N %% 128 == 0");
+  return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qx),
+                                            static_cast<const uint8_t*>(qw), sx, sw,
+                                            static_cast<uint16_t*>(y), M, N, K, M_valid,
+                                            gran == FP8_BLOCK_1x128, 128, as_stream(stream)),
+                    "fp8_linear_fwd");
+}
+
+int fp8_linear_dgrad(const void* qg, const void* qw_t, const float* sg, const float* sw, void* dx,
+                     int64_t M, int64_t N, int64_t K, int64_t M_valid, int gran, void* stream) {
+  int e = check_gemm("fp8_linear_dgrad", qg, qw_t, sg, sw, dx, M, K, N, M_valid, gran);
+  if (e) return e;
+  if (gran == FP8_BLOCK_1x128 && K % 128)
+    return fail(FP8_ERR_SHAPE, "fp8_linear_dgrad: block recipe needs K %% 128 == 0");
+  return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qg),
+                                            static_cast<const uint8_t*>(qw_t), sg, sw,
+                                            static_cast<uint16_t*>(dx), M, K, N, M_valid,
+                                            gran == FP8_BLOCK_1x128, 128, as_stream(stream)),
+                    "fp8_linear_dgrad");
+}
+
+int fp8_linear_wgrad(const void* qg_t, const void* qx_t, const float* sg, const float* sx, void* dw,
+                     int64_t M, int64_t N, int64_t K, int gran, void* stream) {
+  int e = check_gemm("fp8_linear_wgrad", qg_t, qx_t, sg, sx, dw, N, K, M, N, gran);
+  if (e) return e;
+  return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qg_t),
+                                            static_cast<const uint8_t*>(qx_t), sg, sx,
+                                            static_cast<uint16_t*>(dw), N, K, M, N,
+                                            gran == FP8_BLOCK_1x128, 1, as_stream(stream)),
+                    "fp8_linear_wgrad");
+}
+
+int fp8_pad_tokens(const void* x, int64_t T, int64_t cols, int32_t multiple, void* x_pad,
+                   int64_t* T_pad, void* stream) {
+  const char* fn = "fp8_pad_tokens";
+  if (!T_pad) return fail(FP8_ERR_NULL, "%s: T_pad is NULL", fn);
+  if (T < 0 || cols < 0) return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
+  if (multiple < 1) return fail(FP8_ERR_SHAPE, "%s: multiple=%d must be >= 1", fn, multiple);
+  const int64_t pad = ((-T) % multiple + multiple) % multiple;
+  *T_pad = T + pad;
+  if (!x_pad) return ok();
+  if (T * cols > 0 && !x) return fail(FP8_ERR_NULL, "%s: x is NULL", fn);
+  return hip_status(fp8lin::launch_pad_tokens(static_cast<const uint16_t*>(x), T, cols, *T_pad,
+                                              static_cast<uint16_t*>(x_pad), as_stream(stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Device helpers shared by the gfx950 kernels of the scaled FP8 linear layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+constexpr float kE4M3Max = 448.0f;     // largest finite OCP e4m3 value
+constexpr uint32_t kE4M3MaxBits = 0x43E00000u;   // 448.0f
+constexpr uint32_t kF32InfBits = 0x7F800000u;
+constexpr float kAmaxFloor = 1e-12f;   // lower clamp of amax before 448/amax
+
+// bf16 pair packed in a dword -> two floats (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// Saturate |v| > 448 (including +-inf) to +-448, keep NaN as it is. The
+// hardware converter is then only ever given values inside the e4m3 range or
+// NaN, so its own overflow behaviour never matters.
+__device__ __forceinline__ float sat_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t a = u & 0x7FFFFFFFu;
+  bool over = (a > kE4M3MaxBits) & (a <= kF32InfBits);
+  return over ? __uint_as_float((u & 0x80000000u) | kE4M3MaxBits) : v;
+}
+
+// Two floats -> two OCP e4m3 codes (round to nearest even) in bits [15:0]
+// of the result (first argument in the low byte). gfx950's v_cvt_pk_fp8_f32
+// converts to the OCP E4M3 format.
+__device__ __forceinline__ uint32_t cvt2_e4m3(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false) & 0xFFFFu;
+}
+
+// Four floats -> four codes in one dword (a in the low byte).
+__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), lo, true);
+}
+
+// Sign bits of four bf16 values (elements 0,1 in d0, 2,3 in d1) placed at
+// bit 7 of bytes 0..3.
+__device__ __forceinline__ uint32_t sign_bytes(uint32_t d0, uint32_t d1) {
+  return ((d0 >> 8) & 0x80u) | ((d0 >> 16) & 0x8000u) | ((d1 << 8) & 0x800000u) |
+         (d1 & 0x80000000u);
+}
+
+// A NaN product is encoded as 0x7F with the sign of its input. The hardware
+// converter returns 0xFF for every NaN, and saturation keeps finite codes at
+// or below 0xFE, so a 0xFF byte marks exactly the NaN products.
+__device__ __forceinline__ uint32_t fix_nan_codes(uint32_t codes, uint32_t signs) {
+  const uint32_t ff = ((codes & 0x7F7F7F7Fu) + 0x01010101u) & codes & 0x80808080u;
+  if (__builtin_expect(ff != 0u, 0)) {
+    const uint32_t m = (ff >> 7) * 0xFFu;
+    codes = (codes & ~m) | (m & (0x7F7F7F7Fu | signs));
+  }
+  return codes;
+}
+
+// Four bf16 inputs (packed in d0, d1) times their multipliers -> four codes.
+__device__ __forceinline__ uint32_t quant4(uint32_t d0, uint32_t d1, float s0, float s1, float s2,
+                                           float s3) {
+  const uint32_t c = cvt4_e4m3(bf16_lo(d0) * s0, bf16_hi(d0) * s1, bf16_lo(d1) * s2,
+                               bf16_hi(d1) * s3);
+  return fix_nan_codes(c, sign_bytes(d0, d1));
+}
+
+// float -> bf16 bits, round to nearest even; NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > kF32InfBits) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Scale pair from an amax: a = max(amax, 1e-12) keeping NaN, then two IEEE
+// divisions (this translation unit is built without fast-math, so '/' is the
+// correctly rounded float32 division).
+__device__ __forceinline__ void scale_pair(float amax, float* scale, float* scale_inv) {
+  float a = (amax < kAmaxFloor) ? kAmaxFloor : amax;   // NaN < x is false: NaN kept
+  *scale = a / kE4M3Max;
+  *scale_inv = kE4M3Max / a;
+}
+
+// Wavefront (64 lanes) max of an unsigned value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+}  // namespace fp8lin

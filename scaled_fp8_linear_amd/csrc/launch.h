@@ -1,0 +1,37 @@
+// Internal launchers: one per kernel family. Host-side argument checking lives
+// in abi.cpp; these only enqueue work on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+
+hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t rows, int64_t cols,
+                                      int64_t rows_valid, const float* scale_inv, uint8_t* q,
+                                      uint8_t* q_t, float* amax, hipStream_t s);
+
+// Block recipe: 1x128 tiles (activations/gradients), 128x128 tiles (weights).
+hipError_t launch_quantize_block_1x128(const uint16_t* x, int64_t rows, int64_t cols,
+                                       int64_t rows_valid, uint8_t* q, uint8_t* q_t,
+                                       float* amax, float* scale, float* scale_t, hipStream_t s);
+hipError_t launch_quantize_block_128x128(const uint16_t* x, int64_t rows, int64_t cols,
+                                         uint8_t* q, uint8_t* q_t, float* amax, float* scale,
+                                         float* scale_t, hipStream_t s);
+
+hipError_t launch_scale_update(int mode, const float* amax, float* hist, int32_t len,
+                               int32_t pos, float* scale, float* scale_inv, hipStream_t s);
+
+hipError_t launch_pad_tokens(const uint16_t* x, int64_t T, int64_t cols, int64_t T_pad,
+                             uint16_t* x_pad, hipStream_t s);
+
+// D[m,n] = bf16(scale * sum_k A[m,k] * B[n,k]); A [M,K], B [N,K], D [M,N].
+// Tensorwise: scale = sa[0] * sb[0]. Block: sa [M, K/128]; sb [N/b_rows, K/128]
+// with b_rows = 128 (weight tiles) or 1 (1x128 tiles). Rows m >= M_valid of D are 0.
+hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
+                           uint16_t* D, int64_t M, int64_t N, int64_t K, int64_t M_valid,
+                           bool block_scaled, int b_rows_per_scale, hipStream_t s);
+
+}  // namespace fp8lin

@@ -1,0 +1,74 @@
+// Delayed-scaling bookkeeping on the device (no host synchronization).
+//
+// AstrAI, astrai/extension/fp8_state.py:
+//  * _update_delayed_scale: a = clamp_min(amax, 1e-12); scale = a/448,
+//    scale_inv = 448/a, written for the next call;
+//  * FP8TensorMeta.record: hist[idx] = amax (the host keeps idx);
+//  * FP8TensorMeta.refresh: m = max(hist); if m > 0: scale = m/448,
+//    scale_inv = 448/m.
+// Each quotient is one correctly rounded float32 division (no fast-math in
+// this translation unit, so '/' lowers to the IEEE division sequence).
+#include "common.h"
+#include "launch.h"
+
+namespace fp8lin {
+
+namespace {
+
+__global__ void scale_from_amax_kernel(const float* __restrict__ amax, float* __restrict__ scale,
+                                       float* __restrict__ scale_inv) {
+  float s, si;
+  scale_pair(amax[0], &s, &si);
+  scale[0] = s;
+  scale_inv[0] = si;
+}
+
+__global__ void record_kernel(const float* __restrict__ amax, float* __restrict__ hist, int pos) {
+  hist[pos] = amax[0];
+}
+
+// One wavefront; len is small (16 for the pages' schedule).
+__global__ void refresh_kernel(const float* __restrict__ hist, int len, float* __restrict__ scale,
+                               float* __restrict__ scale_inv) {
+  const int lane = threadIdx.x;
+  // max with NaN propagation, as torch.max does: track NaN separately
+  float m = 0.0f;
+  bool any = false, nan = false;
+  for (int i = lane; i < len; i += 64) {
+    float v = hist[i];
+    nan |= (v != v);
+    m = any ? fmaxf(m, v) : v;
+    any = true;
+  }
+  // reduce across the wavefront (lanes with no entry contribute -inf)
+  float r = any ? m : -__builtin_inff();
+  for (int off = 32; off > 0; off >>= 1) r = fmaxf(r, __shfl_xor(r, off, 64));
+  int anynan = __any(nan);
+  if (lane == 0 && !anynan && r > 0.0f) {
+    scale[0] = r / kE4M3Max;
+    scale_inv[0] = kE4M3Max / r;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scale_update(int mode, const float* amax, float* hist, int32_t len,
+                               int32_t pos, float* scale, float* scale_inv, hipStream_t s) {
+  switch (mode) {
+    case 0:
+      hipLaunchKernelGGL(scale_from_amax_kernel, dim3(1), dim3(1), 0, s, amax, scale, scale_inv);
+      break;
+    case 1:
+      hipLaunchKernelGGL(record_kernel, dim3(1), dim3(1), 0, s, amax, hist, (int)pos);
+      break;
+    case 2:
+      hipLaunchKernelGGL(refresh_kernel, dim3(1), dim3(64), 0, s, (const float*)hist, (int)len,
+                         scale, scale_inv);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8lin

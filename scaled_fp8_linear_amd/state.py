@@ -1,0 +1,140 @@
+"""Host-side schedule of delayed scaling for one FP8 linear layer.
+
+This is the bookkeeping of AstrAI's ``fp8_state.py`` (``FP8TensorMeta``,
+``FP8State.step``, ``fp8_linear_forward`` / ``fp8_linear_backward``) laid over
+the C ABI. All arithmetic runs in the library's kernels; this class only owns
+the device tensors that hold the scales and the ring, the host-side ring index
+and step counter, and the order of calls:
+
+    begin_step()   step_count += 1; every 16th step: REFRESH the weight scale
+    forward(x, w)  quantize W (scale_inv), RECORD amax_w, quantize x with the
+                   delayed x scale, forward GEMM, FROM_AMAX(amax_x) -> next slot
+    backward(g)    quantize g with the delayed g scale, dgrad (Qg, Qw^T),
+                   wgrad (Qg^T, Qx^T with the scale that made Qx^T),
+                   FROM_AMAX(amax_g) -> next slot
+    end_step()     the next slots become current
+
+Reading: the activation and gradient scales live in two slots (current,
+next) so that wgrad multiplies Qx^T by the scale that produced it, while the
+update for the next step is written as soon as amax is known. Nothing here
+synchronizes with the device.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _abi
+from ._abi import Slot
+
+
+class _NoProbe:
+    def __call__(self, tag):
+        return self
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+class DelayedScalingLinear:
+    """Delayed scaling for one linear layer (weight meta + activation/gradient scales).
+
+    ``probe(tag)`` may be given to wrap each kernel call in a context manager
+    (the benchmark records HIP events with it); tags are "quantize", "gemm"
+    and "scale".
+    """
+
+    def __init__(self, device, update_interval: int = 16, probe=None):
+        self.probe = probe or _NoProbe()
+        f32 = dict(dtype=torch.float32, device=device)
+        self.update_interval = update_interval
+        self.step_count = 0
+        self.w_scale = torch.ones(1, **f32)
+        self.w_scale_inv = torch.ones(1, **f32)
+        self.hist = torch.ones(update_interval, **f32)
+        self.idx = 0
+        # [slot] pairs for activations and gradients
+        self.x_scale = torch.ones(2, **f32)
+        self.x_scale_inv = torch.ones(2, **f32)
+        self.g_scale = torch.ones(2, **f32)
+        self.g_scale_inv = torch.ones(2, **f32)
+        self.cur = 0
+        self.amax_w = torch.zeros(1, **f32)
+        self.amax_x = torch.zeros(1, **f32)
+        self.amax_g = torch.zeros(1, **f32)
+        self._saved = None
+
+    @property
+    def nxt(self) -> int:
+        return 1 - self.cur
+
+    def begin_step(self, stream=None) -> bool:
+        self.step_count += 1
+        if self.step_count % self.update_interval == 0:
+            with self.probe("scale"):
+                _abi.fp8_scale_update(_abi.FP8_SCALE_REFRESH, hist=self.hist, scale=self.w_scale,
+                                      scale_inv=self.w_scale_inv, stream=stream)
+            return True
+        return False
+
+    def forward(self, x, w, rows_valid=None, out=None, bufs=None, stream=None):
+        """y = x W^T. ``bufs`` may hold preallocated qw, qw_t, qx, qx_t tensors."""
+        b = bufs or {}
+        p = self.probe
+        with p("quantize"):
+            qw, qw_t, _, _, _ = _abi.fp8_quantize_amax(
+                w, scale_inv=self.w_scale_inv, q=b.get("qw"), q_t=b.get("qw_t"), amax=self.amax_w,
+                stream=stream)
+        with p("scale"):
+            _abi.fp8_scale_update(_abi.FP8_SCALE_RECORD, amax=self.amax_w, hist=self.hist,
+                                  pos=self.idx, stream=stream)
+        self.idx = (self.idx + 1) % self.hist.numel()
+        sx, sx_inv = Slot(self.x_scale, self.cur), Slot(self.x_scale_inv, self.cur)
+        with p("quantize"):
+            qx, qx_t, _, _, _ = _abi.fp8_quantize_amax(
+                x, rows_valid=rows_valid, scale_inv=sx_inv, q=b.get("qx"), q_t=b.get("qx_t"),
+                amax=self.amax_x, stream=stream)
+        with p("gemm"):
+            y = _abi.fp8_linear_fwd(qx, qw, sx, self.w_scale, y=out, M_valid=rows_valid,
+                                    stream=stream)
+        with p("scale"):
+            _abi.fp8_scale_update(_abi.FP8_SCALE_FROM_AMAX, amax=self.amax_x,
+                                  scale=Slot(self.x_scale, self.nxt),
+                                  scale_inv=Slot(self.x_scale_inv, self.nxt), stream=stream)
+        self._saved = (qx_t, qw_t, rows_valid)
+        return y
+
+    def backward(self, g, dx=None, dw=None, bufs=None, stream=None):
+        """(dx, dW) for the output gradient g."""
+        b = bufs or {}
+        p = self.probe
+        qx_t, qw_t, rows_valid = self._saved
+        sg, sg_inv = Slot(self.g_scale, self.cur), Slot(self.g_scale_inv, self.cur)
+        with p("quantize"):
+            qg, qg_t, _, _, _ = _abi.fp8_quantize_amax(
+                g, rows_valid=rows_valid, scale_inv=sg_inv, q=b.get("qg"), q_t=b.get("qg_t"),
+                amax=self.amax_g, stream=stream)
+        with p("gemm"):
+            dx = _abi.fp8_linear_dgrad(qg, qw_t, sg, self.w_scale, dx=dx, M_valid=rows_valid,
+                                       stream=stream)
+        with p("gemm"):
+            dw = _abi.fp8_linear_wgrad(qg_t, qx_t, sg, Slot(self.x_scale, self.cur), dw=dw,
+                                       stream=stream)
+        with p("scale"):
+            _abi.fp8_scale_update(_abi.FP8_SCALE_FROM_AMAX, amax=self.amax_g,
+                                  scale=Slot(self.g_scale, self.nxt),
+                                  scale_inv=Slot(self.g_scale_inv, self.nxt), stream=stream)
+        return dx, dw
+
+    def end_step(self) -> None:
+        self.cur = self.nxt
+
+    def state(self) -> dict:
+        """Host copies of the schedule state (synchronizes; for tests)."""
+        c = self.cur
+        return dict(step=self.step_count, idx=self.idx, hist=self.hist.cpu().numpy().copy(),
+                    w_scale=self.w_scale.item(), w_scale_inv=self.w_scale_inv.item(),
+                    x_scale=self.x_scale[c].item(), x_scale_inv=self.x_scale_inv[c].item(),
+                    g_scale=self.g_scale[c].item(), g_scale_inv=self.g_scale_inv[c].item())

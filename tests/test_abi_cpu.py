@@ -1,0 +1,94 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects bad
+arguments with the documented status before touching the GPU (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8lin.h")
+LIB = os.path.join(ROOT, "scaled_fp8_linear_amd", "libfp8lin.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(fp8_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libfp8lin.so not built (python -m scaled_fp8_linear_amd.build)")
+    import scaled_fp8_linear_amd as m
+    return m.load()
+
+
+def test_header_declares_the_six_calls():
+    names = _declared()
+    for n in ("fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
+              "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_version(lib):
+    assert lib.fp8_version().decode().startswith("fp8lin")
+
+
+def _err(lib):
+    return lib.fp8_last_error().decode()
+
+
+def test_token_count_not_multiple_of_16(lib):
+    # SpecForge PR 2 quotes a token count of 3858, which float8 GEMMs reject.
+    assert lib.fp8_linear_fwd(None, None, None, None, None, 3858, 4096, 4096, 3858, 0, None) == 2
+    assert "3858" in _err(lib) and "16" in _err(lib)
+    assert lib.fp8_linear_wgrad(None, None, None, None, None, 3858, 4096, 4096, 0, None) == 2
+
+
+def test_gemm_argument_checks(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.fp8_linear_fwd(p, p, p, p, None, 16, 16, 16, 16, 0, None) == 1        # NULL y
+    assert lib.fp8_linear_fwd(p, p, p, p, ctypes.c_void_p(8), 16, 16, 16, 16, 0, None) == 3
+    assert lib.fp8_linear_fwd(p, p, p, p, p, 16, 16, 16, 17, 0, None) == 2           # M_valid > M
+    assert lib.fp8_linear_fwd(p, p, p, p, p, 16, 16, 16, 16, 9, None) == 4           # granularity
+    assert lib.fp8_linear_fwd(p, p, p, p, p, 16, 16, 1 << 17, 16, 0, None) == 4      # K too long
+    assert lib.fp8_linear_dgrad(p, p, p, p, p, 16, 16, -16, 16, 0, None) == 2
+    assert lib.fp8_linear_fwd(p, p, p, p, p, 16, 16, 48, 16, 1, None) == 2           # block K%128
+
+
+def test_quantize_argument_checks(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.fp8_quantize_amax(None, 16, 16, 16, 0, p, p, p, p, None, None, None) == 1
+    assert lib.fp8_quantize_amax(p, 24, 16, 24, 0, p, p, p, p, None, None, None) == 2
+    assert lib.fp8_quantize_amax(p, 16, 16, 17, 0, p, p, p, p, None, None, None) == 2
+    assert lib.fp8_quantize_amax(p, 16, 16, 16, 0, None, p, None, p, None, None, None) == 1
+    assert lib.fp8_quantize_amax(p, 16, 16, 16, 0, p, p, None, p, p, None, None) == 4
+    assert lib.fp8_quantize_amax(p, 128, 128, 128, 1, p, p, None, None, p, None, None) == 4
+    assert lib.fp8_quantize_amax(p, 128, 128, 128, 1, None, p, None, None, None, None, None) == 1
+    assert lib.fp8_quantize_amax(p, 128, 128, 64, 2, None, p, None, None, p, None, None) == 2
+    assert lib.fp8_quantize_amax(p, 16, 16, 16, 7, None, None, None, None, None, None, None) == 2
+
+
+def test_scale_update_argument_checks(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.fp8_scale_update(0, None, None, 0, 0, p, p, None) == 1
+    assert lib.fp8_scale_update(1, p, p, 16, 16, None, None, None) == 2
+    assert lib.fp8_scale_update(2, None, p, 0, 0, p, p, None) == 2
+    assert lib.fp8_scale_update(5, p, p, 16, 0, p, p, None) == 4
+
+
+def test_pad_tokens_query(lib):
+    out = ctypes.c_int64(-1)
+    for T, mult, want in ((3858, 16, 3872), (0, 16, 0), (16, 16, 16), (1, 16, 16), (67827, 16, 67840),
+                          (5, 8, 8)):
+        assert lib.fp8_pad_tokens(None, T, 4096, mult, None, ctypes.byref(out), None) == 0
+        assert out.value == want
+    assert lib.fp8_pad_tokens(None, 5, 8, 0, None, ctypes.byref(out), None) == 2
+    assert lib.fp8_pad_tokens(None, 5, 8, 16, None, None, None) == 1

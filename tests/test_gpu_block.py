@@ -1,0 +1,86 @@
+"""GPU parity for the block-scaled recipe: 1x128 / 128x128 tile quantize bit-exact (codes, tile
+amaxes, tile scales, and the transposed copy re-quantized along tokens), and the per-block
+scaled GEMMs within the tolerance."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import block
+from tests.gpu_util import (assert_same_bytes, assert_within, dev_bf16, host_bf16_f64, host_u8,
+                            note)
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_fp8_linear_amd as m
+    m.load()
+    return m
+
+
+def _bits32(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+def _f32_equal(got, want, what):
+    assert got.shape == want.shape, what
+    g, w = _bits32(got), _bits32(want)
+    bad = np.flatnonzero(g.ravel() != w.ravel())
+    assert bad.size == 0, f"{what}: {bad.size} differ, first {got.ravel()[bad[0]]} vs {want.ravel()[bad[0]]}"
+
+
+@pytest.mark.parametrize("rows,cols,rv", [(128, 128, 128), (384, 256, 300), (256, 640, 1)])
+def test_quantize_1x128(lib, rows, cols, rv):
+    x = workloads.bf16_tensor("outlier_normal", (rows, cols), 5, rows + cols, 0, rate=0.01, mult=100.0)
+    x[rv:] = 0x7FC0
+    note(f"block 1x128 quantize {rows}x{cols} rv={rv}")
+    q, qt, a, s, st = lib.fp8_quantize_amax(dev_bf16(x), rows_valid=rv, gran=lib.FP8_BLOCK_1x128)
+    torch.cuda.synchronize()
+    oq, oqt, oa, os_, ost = block.quantize_1x128(x, rv)
+    assert_same_bytes(host_u8(q), oq, "q")
+    assert_same_bytes(host_u8(qt), oqt, "q_t")
+    _f32_equal(a.cpu().numpy(), oa, "tile amax")
+    _f32_equal(s.cpu().numpy(), os_, "row-tile scales")
+    _f32_equal(st.cpu().numpy(), ost, "column-tile scales")
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256)])
+def test_quantize_128x128(lib, rows, cols):
+    w = workloads.bf16_tensor("outlier_normal", (rows, cols), 5, 7 + rows, 0, rate=0.01, mult=100.0)
+    note(f"block 128x128 quantize {rows}x{cols}")
+    q, qt, a, s, st = lib.fp8_quantize_amax(dev_bf16(w), gran=lib.FP8_BLOCK_128x128)
+    torch.cuda.synchronize()
+    oq, oqt, oa, os_, ost = block.quantize_128x128(w)
+    assert_same_bytes(host_u8(q), oq, "q")
+    assert_same_bytes(host_u8(qt), oqt, "q_t")
+    _f32_equal(a.cpu().numpy(), oa, "tile amax")
+    _f32_equal(s.cpu().numpy(), os_, "scales")
+    _f32_equal(st.cpu().numpy(), ost, "transposed scales")
+
+
+@pytest.mark.parametrize("M,K,N,rv", [(256, 256, 384, 256), (384, 512, 256, 300)])
+def test_block_linear_step(lib, M, K, N, rv):
+    d = workloads.linear_inputs(5, 0, M=M, K=K, N=N)
+    x, w, g = d["x"], d["w"], d["g"]
+    note(f"block recipe step M={M} K={K} N={N}")
+    B = lib.FP8_BLOCK_1x128
+    qx, qx_t, _, sx, sx_t = lib.fp8_quantize_amax(dev_bf16(x), rows_valid=rv, gran=B)
+    qw, qw_t, _, sw, sw_t = lib.fp8_quantize_amax(dev_bf16(w), gran=lib.FP8_BLOCK_128x128)
+    qg, qg_t, _, sg, sg_t = lib.fp8_quantize_amax(dev_bf16(g), rows_valid=rv, gran=B)
+    y = lib.fp8_linear_fwd(qx, qw, sx, sw, M_valid=rv, gran=B)
+    dx = lib.fp8_linear_dgrad(qg, qw_t, sg, sw_t, M_valid=rv, gran=B)
+    dw = lib.fp8_linear_wgrad(qg_t, qx_t, sg_t, sx_t, gran=B)
+    torch.cuda.synchronize()
+    r = __import__("oracle.linear", fromlist=["x"]).block_linear_step(x, w, g, rv)
+    assert_same_bytes(host_u8(qx_t), r["qx_t"], "qx_t")
+    assert_same_bytes(host_u8(qg_t), r["qg_t"], "qg_t")
+    yb = block.block_error_bound(r["qx"], r["qw"], r["sx"], r["sw"], 128)
+    assert_within(host_bf16_f64(y), r["y"], yb, "block fwd")
+    db = block.block_error_bound(r["qg"], r["qw_t"], r["sg"], r["sw_t"], 128)
+    assert_within(host_bf16_f64(dx), r["dx"], db, "block dgrad")
+    wb = block.block_error_bound(r["qg_t"], r["qx_t"], r["sg_t"], r["sx_t"], 1)
+    assert_within(host_bf16_f64(dw), r["dw"], wb, "block wgrad")

@@ -1,0 +1,141 @@
+"""GPU parity: the scaled FP8 GEMMs (forward, dgrad, wgrad) against the exact float64 oracle.
+
+Tolerance (per element): |D_gpu - D| <= 1e-2 * ||dqA[m,:]||_2 * ||dqB[n,:]||_2, the target
+stated for the method, with D the exact result and dq the dequantized operands. The GPU result
+is float32-accumulated and rounded to bf16, which keeps it orders of magnitude inside that
+bound; the tests also report the worst ratio.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import e4m3, gemm
+from oracle.quantize import quantize_tensorwise
+from oracle.scaling import scale_from_amax
+from oracle.quantize import amax as o_amax
+from tests.gpu_util import assert_within, dev_f32, host_bf16_f64, note
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_fp8_linear_amd as m
+    m.load()
+    return m
+
+
+def _codes(shape, seed, kind="normal", **p):
+    """Random e4m3 operands: quantize seeded bf16 data with its current scale (oracle)."""
+    bits = workloads.bf16_tensor(kind, shape, 70, seed, 0, **p)
+    s, si = scale_from_amax(o_amax(bits))
+    q, _, _ = quantize_tensorwise(bits, si)
+    return q, s
+
+
+def _dev(q):
+    return torch.from_numpy(np.ascontiguousarray(q)).cuda()
+
+
+def _exact_and_bound(qa, qb, sa, sb):
+    return gemm.scaled_gemm(qa, qb, sa, sb), gemm.error_bound(qa, qb, sa, sb)
+
+
+SHAPES = [(64, 128, 128), (16, 16, 16), (528, 784, 656), (256, 256, 4096), (1040, 272, 1008),
+          (4096 + 16, 512, 144)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_forward(lib, M, N, K):
+    qa, sa = _codes((M, K), 1 + M, "student_t", nu=3)
+    qb, sb = _codes((N, K), 2 + N, "normal", std=0.02)
+    note(f"fp8_linear_fwd M={M} N={N} K={K}")
+    y = lib.fp8_linear_fwd(_dev(qa), _dev(qb), dev_f32(sa), dev_f32(sb))
+    torch.cuda.synchronize()
+    D, bound = _exact_and_bound(qa, qb, sa, sb)
+    worst = assert_within(host_bf16_f64(y), D, bound, f"fwd {M}x{N}x{K}")
+    # the bf16 output rounding alone can use 2**-9 / 1e-2 ~ 0.2 of the bound (|D| <= ||a|| ||b||)
+    assert worst < 0.25
+
+
+@pytest.mark.parametrize("M,N,K", [(528, 784, 656), (64, 128, 128)])
+def test_dgrad_and_wgrad(lib, M, N, K):
+    """dgrad = Qg . Qw (via Qw^T), wgrad = Qg^T . Qx (via both transposed copies)."""
+    qg, sg = _codes((M, N), 3 + M, "normal", std=1e-3)
+    qw, sw = _codes((N, K), 4 + N, "normal", std=0.02)
+    qx, sx = _codes((M, K), 5 + K, "student_t", nu=3)
+    qw_t, qg_t, qx_t = (np.ascontiguousarray(a.T) for a in (qw, qg, qx))
+    note(f"fp8_linear_dgrad M={M} N={N} K={K}")
+    dx = lib.fp8_linear_dgrad(_dev(qg), _dev(qw_t), dev_f32(sg), dev_f32(sw))
+    note(f"fp8_linear_wgrad M={M} N={N} K={K}")
+    dw = lib.fp8_linear_wgrad(_dev(qg_t), _dev(qx_t), dev_f32(sg), dev_f32(sx))
+    torch.cuda.synchronize()
+    assert tuple(dx.shape) == (M, K) and tuple(dw.shape) == (N, K)
+    D, b = _exact_and_bound(qg, qw_t, sg, sw)
+    assert_within(host_bf16_f64(dx), D, b, "dgrad")
+    D, b = _exact_and_bound(qg_t, qx_t, sg, sx)
+    assert_within(host_bf16_f64(dw), D, b, "wgrad")
+
+
+def test_m_valid_rows_are_zero(lib):
+    M, N, K = 272, 256, 128
+    qa, sa = _codes((M, K), 11, std=1.0)
+    qb, sb = _codes((N, K), 12, std=1.0)
+    note("fp8_linear_fwd with M_valid=200")
+    y = lib.fp8_linear_fwd(_dev(qa), _dev(qb), dev_f32(sa), dev_f32(sb), M_valid=200)
+    note("fp8_linear_dgrad with M_valid=200")
+    dx = lib.fp8_linear_dgrad(_dev(qa), _dev(qb), dev_f32(sa), dev_f32(sb), M_valid=200)
+    torch.cuda.synchronize()
+    yh, dxh = host_bf16_f64(y), host_bf16_f64(dx)
+    assert np.all(yh[200:] == 0) and np.all(dxh[200:] == 0)
+    D, b = _exact_and_bound(qa[:200], qb, sa, sb)
+    assert_within(yh[:200], D, b, "fwd valid rows")
+
+
+def test_special_operands(lib):
+    """All-448 operands at K=4096 (largest partial sums), zeros, and signed zeros."""
+    M = N = 128
+    K = 4096
+    qa = np.full((M, K), 0x7E, np.uint8)
+    qa[1::2] = 0xFE
+    qb = np.full((N, K), 0x7E, np.uint8)
+    qb[:, ::3] = 0x80
+    qb[5] = 0
+    note("fp8_linear_fwd saturated operands")
+    y = lib.fp8_linear_fwd(_dev(qa), _dev(qb), dev_f32(1 / 448), dev_f32(1 / 448))
+    torch.cuda.synchronize()
+    D, b = _exact_and_bound(qa, qb, np.float32(1 / 448), np.float32(1 / 448))
+    assert_within(host_bf16_f64(y), D, b, "saturated")
+    assert np.all(host_bf16_f64(y)[:, 5] == 0)
+
+
+def test_full_size_headline_sampled(lib):
+    """The MLP block's gate/up forward at M=8192, K=4096, N=14336 (the launch configuration the
+    benchmark times): 2048 sampled outputs computed one by one by the oracle."""
+    M, K, N = 8192, 4096, 14336
+    x = workloads.bf16_tensor("student_t", (M, K), 3, workloads.T_X, 0, nu=3)
+    w = workloads.bf16_tensor("normal", (N, K), 3, workloads.T_WGATE, 0, std=0.02)
+    sx, sxi = scale_from_amax(o_amax(x))
+    sw, swi = scale_from_amax(o_amax(w))
+    note("full size: quantize x, w on the GPU")
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    wd = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16)
+    qx, _, _, _, _ = lib.fp8_quantize_amax(xd, scale_inv=dev_f32(sxi), want_q_t=False)
+    qw, _, _, _, _ = lib.fp8_quantize_amax(wd, scale_inv=dev_f32(swi), want_q_t=False)
+    note("full size: fp8_linear_fwd 8192x14336x4096")
+    y = lib.fp8_linear_fwd(qx, qw, dev_f32(sx), dev_f32(sw))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    ms = rng.integers(0, M, 2048)
+    ns = rng.integers(0, N, 2048)
+    yh = host_bf16_f64(y)
+    from oracle.quantize import quantize_values
+    for m, n in zip(ms, ns):
+        a = quantize_values(x[m:m + 1], sxi)
+        bq = quantize_values(w[n:n + 1], swi)
+        D = gemm.scaled_gemm(a, bq, sx, sw)[0, 0]
+        bound = gemm.error_bound(a, bq, sx, sb=sw)[0, 0]
+        assert abs(yh[m, n] - D) <= bound, (m, n, yh[m, n], D, bound)

@@ -142,3 +142,22 @@ def test_activation_and_grad_scales_are_one_step_late():
             assert (f["sx"], f["sx_inv"]) == scaling.scale_from_amax(prev[0])
             assert (b["sg"], b["sg_inv"]) == scaling.scale_from_amax(prev[1])
         prev = (f["amax_x"], b["amax_g"])
+
+
+def test_scales_only_step_follows_the_full_step():
+    """The GEMM-free bookkeeping used for long full-size runs tracks forward/backward exactly."""
+    import workloads
+    full, lite = DelayedLinear(), DelayedLinear()
+    w = workloads.linear_inputs(2, 0, M=32, K=32, N=16)["w"]
+    for t in range(1, 35):
+        d = workloads.linear_inputs(2, t, M=32, K=32, N=16)
+        full.begin_step()
+        lite.begin_step()
+        f = full.forward(d["x"], w, rows_valid=30)
+        b = full.backward(d["g"])
+        u = lite.scales_only_step(d["x"], w, d["g"], rows_valid=30)
+        assert (u["sx"], u["sw"], u["sg"]) == (f["sx"], f["sw"], b["sg"])
+        assert (u["sx_inv"], u["sw_inv"], u["sg_inv"]) == (f["sx_inv"], f["sw_inv"], b["sg_inv"])
+        s1, s2 = full.state(), lite.state()
+        assert np.array_equal(s1.pop("hist"), s2.pop("hist")) and s1 == s2
+        w = workloads.drift(w, 2, t, 1e-4)
