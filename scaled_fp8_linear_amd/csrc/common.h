@@ -65,6 +65,14 @@ __device__ __forceinline__ uint32_t quant4(uint32_t d0, uint32_t d1, float s0, f
   return fix_nan_codes(c, sign_bytes(d0, d1));
 }
 
+// Two floats -> two bf16 in one dword (a in the low half), round to nearest even
+// (gfx950's v_cvt_pk_bf16_f32).
+typedef __bf16 fp8lin_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const fp8lin_bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // float -> bf16 bits, round to nearest even; NaN -> quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
