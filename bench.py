@@ -40,7 +40,23 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 512 MiB buffer three times (for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of known size: the reference for FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    nbytes = 512 << 20
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": nbytes,
+                                           "bytes_written_per_copy": nbytes, "copies": 3}}))
 
 
 class EventProbe:
@@ -133,6 +149,10 @@ def main():
         print(json.dumps({"error": "this build measures one GPU: the hot path runs on one "
                                    "device and has no cross-GPU step; run with --gpus 1"}))
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 

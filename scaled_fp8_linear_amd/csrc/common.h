@@ -11,6 +11,23 @@ constexpr uint32_t kE4M3MaxBits = 0x43E00000u;   // 448.0f
 constexpr uint32_t kF32InfBits = 0x7F800000u;
 constexpr float kAmaxFloor = 1e-12f;   // lower clamp of amax before 448/amax
 
+// Streaming (non-temporal) 16/8-byte loads and stores: the quantize pass reads and
+// writes every byte once, so it keeps them out of the caches' reuse set.
+typedef unsigned fp8lin_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned fp8lin_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const fp8lin_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const fp8lin_u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_stream16(void* p, uint4 v) {
+  const fp8lin_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<fp8lin_u32x4*>(p));
+}
+__device__ __forceinline__ void st_stream8(void* p, uint32_t a, uint32_t b) {
+  const fp8lin_u32x2 w = {a, b};
+  __builtin_nontemporal_store(w, reinterpret_cast<fp8lin_u32x2*>(p));
+}
+
 // bf16 pair packed in a dword -> two floats (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }

@@ -500,6 +500,8 @@ struct Persist {
   static constexpr int kStoresPerLane = C::TM * C::TN * 2;   // 16-byte stores per lane
 };
 
+bool xcd_split_enabled();
+
 template <class C>
 __device__ __forceinline__ void tile_coords(int lid, int tiles_m, int tiles_n, int& m0, int& n0) {
   const int per_group = C::GROUP_M * tiles_n;
@@ -516,7 +518,7 @@ __global__ void __launch_bounds__(C::kThreads, 1)
 gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                         const float* __restrict__ sa, const float* __restrict__ sb,
                         uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
-                        int tiles_n) {
+                        int tiles_n, int split_m, int split_n) {
   constexpr int SB = C::kStageBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t s0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[SB];
@@ -529,22 +531,36 @@ gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // ---- this workgroup's tiles: lid = first + i * stride, i < count
-  const int tiles = tiles_m * tiles_n;
+  // ---- this workgroup's tiles: i-th tile = (bm0 + lm, bn0 + ln) of its XCD's block
+  // With split_m * split_n = 8 the tile grid is cut into 8 rectangles, one per XCD
+  // (workgroup b runs on XCD b % 8); the workgroups of an XCD take the rectangle's
+  // tiles in turn, in groups of GROUP_M rows, so the tiles running at the same time
+  // on an XCD are neighbours in both directions. split_m == 0: one rectangle.
   const int nwg = gridDim.x;
-  int first, stride, count;
-  if ((nwg & 7) == 0 && nwg < tiles) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = nwg >> 3;
-    const int chunk = (tiles + 7) >> 3;
-    const int lo = xcd * chunk, hi = min(tiles, lo + chunk);
-    first = lo + slot;
-    stride = per_xcd;
-    count = first < hi ? (hi - first + stride - 1) / stride : 0;
-  } else {
-    first = blockIdx.x;
-    stride = nwg;
-    count = first < tiles ? (tiles - first + stride - 1) / stride : 0;
+  int bm0 = 0, bn0 = 0, bmc = tiles_m, bnc = tiles_n, slot = blockIdx.x, nslots = nwg;
+  if (split_m > 0) {
+    const int xcd = blockIdx.x & 7;
+    const int rm = (tiles_m + split_m - 1) / split_m, rn = (tiles_n + split_n - 1) / split_n;
+    const int bx = xcd / split_n, by = xcd % split_n;
+    bm0 = bx * rm;
+    bn0 = by * rn;
+    bmc = max(0, min(tiles_m, bm0 + rm) - bm0);
+    bnc = max(0, min(tiles_n, bn0 + rn) - bn0);
+    slot = blockIdx.x >> 3;
+    nslots = nwg >> 3;
   }
+  const int block_tiles = bmc * bnc;
+  const int count = slot < block_tiles ? (block_tiles - slot + nslots - 1) / nslots : 0;
+  auto tile_mn = [&](int ti, int& m0, int& n0) {
+    const int lid = slot + ti * nslots;
+    const int per_group = C::GROUP_M * bnc;
+    const int group = lid / per_group;
+    const int first_m = group * C::GROUP_M;
+    const int gsize = min(bmc - first_m, C::GROUP_M);
+    const int in_group = lid - group * per_group;
+    m0 = (bm0 + first_m + in_group % gsize) * C::BM;
+    n0 = (bn0 + in_group / gsize) * C::BN;
+  };
   const int nk = (K + kBKS - 1) / kBKS;
 
   const v4i rsA = make_rsrc(A, (uint32_t)(M * K));
@@ -559,7 +575,7 @@ gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict
   auto tile_base = [&](int ti) -> TileBase {
     if (ti >= count) return {kOutOfRange, kOutOfRange};
     int m0, n0;
-    tile_coords<C>(first + ti * stride, tiles_m, tiles_n, m0, n0);
+    tile_mn(ti, m0, n0);
     return {(uint32_t)(m0 + r0) * (uint32_t)K + 16u * ch, (uint32_t)(n0 + r0) * (uint32_t)K + 16u * ch};
   };
   auto issue = [&](uint8_t* stage, TileBase tb, int kstep) {
@@ -619,7 +635,7 @@ gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict
   const float s = sa[0] * sb[0];
   auto epilogue = [&](int ti) {
     int m0, n0;
-    tile_coords<C>(first + ti * stride, tiles_m, tiles_n, m0, n0);
+    tile_mn(ti, m0, n0);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
       const int m = m0 + wm * C::WTM + 32 * i + fr;
@@ -706,9 +722,20 @@ hipError_t run_persist(const uint8_t* A, const uint8_t* B, const float* sa, cons
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + C::BN - 1) / C::BN;
   const int tiles = tiles_m * tiles_n;
-  const int grid = tiles < max_wg ? tiles : max_wg;
+  int grid = tiles < max_wg ? tiles : max_wg;
+  // one rectangle of tiles per XCD: the split with the fewest A+B panel rows per XCD
+  int split_m = 0, split_n = 0;
+  if (grid == max_wg && (max_wg & 7) == 0 && xcd_split_enabled()) {
+    int best = 1 << 30;
+    for (int pm = 1; pm <= 8; pm *= 2) {
+      const int pn = 8 / pm;
+      if (tiles_m % pm || tiles_n % pn) continue;
+      const int cost = (tiles_m / pm) * C::BM + (tiles_n / pn) * C::BN;
+      if (cost < best) { best = cost; split_m = pm; split_n = pn; }
+    }
+  }
   hipLaunchKernelGGL(gemm_fp8_persist_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
-                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n);
+                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   return hipGetLastError();
 }
 
@@ -730,6 +757,14 @@ using CfgBig8 = Cfg<256, 256, 2, 4, 0, 8, false>;     // 8 waves, 128x64 per wav
 using CfgBig4S = Cfg<256, 256, 2, 2, 1, 8, false>;    // swizzle for 64 banks
 using CfgMid = Cfg<128, 128, 2, 2, 0, 8, false>;      // small problems
 using CfgBlk = Cfg<128, 128, 2, 2, 0, 8, true>;       // block recipe
+
+bool xcd_split_enabled() {
+  static bool v = [] {
+    const char* e = getenv("FP8LIN_GEMM_XCD_SPLIT");
+    return e ? atoi(e) != 0 : true;
+  }();
+  return v;
+}
 
 int forced_cfg() {
   static int v = [] {

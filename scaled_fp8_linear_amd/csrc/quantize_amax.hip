@@ -19,6 +19,8 @@
 //    and NaN patterns sort above infinity), reduced across the wavefront with
 //    shuffles, across the workgroup in LDS, and published with ONE atomicMax
 //    per workgroup on the float bits (non-negative floats order as integers).
+#include <stdlib.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -26,24 +28,54 @@ namespace fp8lin {
 
 namespace {
 
-constexpr int kQTR = 128;   // tile rows
-constexpr int kQTC = 256;   // tile cols
-constexpr int kQThreads = 256;
-constexpr int kColDwords = kQTR / 4;   // dwords per transposed column piece
+// Tile of TR rows x TC columns per workgroup of THREADS lanes; NT: streaming
+// (non-temporal) memory accesses.
+template <int TR, int TC, int THREADS, bool NT>
+struct QCfg {
+  static constexpr int kQTR = TR, kQTC = TC, kQThreads = THREADS;
+  static constexpr bool kNT = NT;
+  static constexpr int kColDwords = TR / 4;          // dwords per transposed column piece
+  static constexpr int kChunks = TC / 8;             // 8-column chunks per tile row
+  static constexpr int kGroups = THREADS / kChunks;  // 4-row groups per pass
+  static constexpr int kRowsPerPass = 4 * kGroups;
+  static constexpr int kPasses = TR / kRowsPerPass;
+  static_assert(THREADS % kChunks == 0 && TR % kRowsPerPass == 0, "tile shape");
+};
 
 // Physical dword slot of logical dword `i` of column `c` in the LDS tile.
-// XOR with the column's lane index spreads the 32 lanes that store the same
-// logical dword over 32 banks.
+// XOR with the column's chunk index spreads the lanes that store the same
+// logical dword over the banks.
+template <int COLDW>
 __device__ __forceinline__ int lds_slot(int c, int i) {
-  return c * kColDwords + (i ^ ((c >> 3) & (kColDwords - 1)));
+  return c * COLDW + (i ^ ((c >> 3) & (COLDW - 1)));
 }
 
-__global__ void __launch_bounds__(kQThreads)
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  if constexpr (NT) return ld_stream16(p);
+  else return *reinterpret_cast<const uint4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  if constexpr (NT) st_stream16(p, v);
+  else *reinterpret_cast<uint4*>(p) = v;
+}
+template <bool NT>
+__device__ __forceinline__ void st8(void* p, uint32_t a, uint32_t b) {
+  if constexpr (NT) st_stream8(p, a, b);
+  else *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
+}
+
+template <class QC>
+__global__ void __launch_bounds__(QC::kQThreads)
 quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                            int64_t rows_valid, const float* __restrict__ scale_inv_p,
                            uint8_t* __restrict__ q, uint8_t* __restrict__ q_t,
                            uint32_t* __restrict__ amax_bits, int64_t tiles_c) {
-  __shared__ uint32_t tile_t[kQTC * kColDwords];   // 32 KiB
+  constexpr int kQTR = QC::kQTR, kQTC = QC::kQTC, kQThreads = QC::kQThreads;
+  constexpr int kColDwords = QC::kColDwords;
+  constexpr bool NT = QC::kNT;
+  __shared__ uint32_t tile_t[kQTC * kColDwords];
   __shared__ uint32_t wave_max[kQThreads / 64];
 
   const int t = threadIdx.x;
@@ -54,67 +86,83 @@ quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t
   const bool want_codes = want_q | want_t;
   const float s = want_codes ? *scale_inv_p : 1.0f;
 
-  const int cc = t & 31;          // 8-column chunk inside the tile
-  const int rg = t >> 5;          // row group (0..7)
+  const int cc = t % QC::kChunks;   // 8-column chunk inside the tile
+  const int rg = t / QC::kChunks;   // 4-row group
   const int64_t col = col0 + 8 * cc;
   const bool col_ok = col < cols;
-  uint32_t mx = 0;
+  constexpr int kPasses = QC::kPasses;
+  constexpr int kRPP = QC::kRowsPerPass;
 
+  // All 16 loads of the lane go out before any is used. Rows past rows_valid and
+  // columns past cols are loaded from a clamped (valid) address and zeroed after the
+  // load, so the loads need no branches; rows_valid >= 1 here (the host skips empty
+  // tensors and tiles with no valid row read nothing).
+  const int64_t last_row = rows_valid - 1;
+  const int64_t lcol = col_ok ? col : cols - 8;
+  uint4 v[kPasses][4];
+  bool ok[kPasses][4];
 #pragma unroll
-  for (int p = 0; p < kQTR / 32; ++p) {
-    const int lr = 32 * p + 4 * rg;        // first of 4 consecutive tile rows
-    uint4 v[4];
-    bool ok[4];
+  for (int p = 0; p < kPasses; ++p)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t r = row0 + lr + i;
-      ok[i] = col_ok && (r < rows_valid);
-      v[i] = ok[i] ? *reinterpret_cast<const uint4*>(x + r * cols + col) : make_uint4(0, 0, 0, 0);
+      const int64_t r = row0 + kRPP * p + 4 * rg + i;
+      ok[p][i] = col_ok && (r < rows_valid);
+      const int64_t lr = r < rows_valid ? r : last_row;
+      v[p][i] = ld16<NT>(x + lr * cols + lcol);
     }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t m0 = v[i].x & 0x7FFF7FFFu, m1 = v[i].y & 0x7FFF7FFFu;
-      uint32_t m2 = v[i].z & 0x7FFF7FFFu, m3 = v[i].w & 0x7FFF7FFFu;
-      uint32_t a = max(max(m0 & 0xFFFFu, m0 >> 16), max(m1 & 0xFFFFu, m1 >> 16));
-      uint32_t b = max(max(m2 & 0xFFFFu, m2 >> 16), max(m3 & 0xFFFFu, m3 >> 16));
+      if (!ok[p][i]) v[p][i] = make_uint4(0, 0, 0, 0);
+      const uint32_t m0 = v[p][i].x & 0x7FFF7FFFu, m1 = v[p][i].y & 0x7FFF7FFFu;
+      const uint32_t m2 = v[p][i].z & 0x7FFF7FFFu, m3 = v[p][i].w & 0x7FFF7FFFu;
+      const uint32_t a = max(max(m0 & 0xFFFFu, m0 >> 16), max(m1 & 0xFFFFu, m1 >> 16));
+      const uint32_t b = max(max(m2 & 0xFFFFu, m2 >> 16), max(m3 & 0xFFFFu, m3 >> 16));
       mx = max(mx, max(a, b));
     }
-    if (!want_codes) continue;
-    uint32_t lo[4], hi[4];   // codes of columns 0..3 / 4..7 of each row
+
+  if (want_codes) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo[i] = quant4(v[i].x, v[i].y, s, s, s, s);
-      hi[i] = quant4(v[i].z, v[i].w, s, s, s, s);
-      if (!ok[i]) { lo[i] = 0u; hi[i] = 0u; }      // padding rows are written as 0x00
-    }
-    if (want_q) {
+    for (int p = 0; p < kPasses; ++p) {
+      const int lr = kRPP * p + 4 * rg;      // first of 4 consecutive tile rows
+      uint32_t lo[4], hi[4];   // codes of columns 0..3 / 4..7 of each row
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t r = row0 + lr + i;
-        if (col_ok && r < rows)
-          *reinterpret_cast<uint2*>(q + r * cols + col) = make_uint2(lo[i], hi[i]);
+        lo[i] = quant4(v[p][i].x, v[p][i].y, s, s, s, s);
+        hi[i] = quant4(v[p][i].z, v[p][i].w, s, s, s, s);
+        if (!ok[p][i]) { lo[i] = 0u; hi[i] = 0u; }      // padding rows are written as 0x00
       }
-    }
-    if (want_t) {
-      // 4x4 byte transposes: column j of the chunk gets bytes j of rows 0..3.
+      if (want_q) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const uint32_t* w = half ? hi : lo;
-        // interleave bytes of rows (0,1) and (2,3), then the 16-bit halves
-        uint32_t a01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
-        uint32_t b01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
-        uint32_t a23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
-        uint32_t b23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
-        uint32_t c0 = __builtin_amdgcn_perm(a23, a01, 0x05040100u);     // col 0: r0 r1 r2 r3
-        uint32_t c1 = __builtin_amdgcn_perm(a23, a01, 0x07060302u);     // col 1
-        uint32_t c2 = __builtin_amdgcn_perm(b23, b01, 0x05040100u);     // col 2
-        uint32_t c3 = __builtin_amdgcn_perm(b23, b01, 0x07060302u);     // col 3
-        const int cb = 8 * cc + 4 * half;
-        const int di = lr >> 2;
-        tile_t[lds_slot(cb + 0, di)] = c0;
-        tile_t[lds_slot(cb + 1, di)] = c1;
-        tile_t[lds_slot(cb + 2, di)] = c2;
-        tile_t[lds_slot(cb + 3, di)] = c3;
+        for (int i = 0; i < 4; ++i) {
+          const int64_t r = row0 + lr + i;
+          if (col_ok && r < rows)
+            st8<NT>(q + r * cols + col, lo[i], hi[i]);
+        }
+      }
+      if (want_t) {
+        // 4x4 byte transposes: column j of the chunk gets bytes j of rows 0..3.
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t* w = half ? hi : lo;
+          // interleave bytes of rows (0,1) and (2,3), then the 16-bit halves
+          uint32_t a01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
+          uint32_t b01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
+          uint32_t a23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+          uint32_t b23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+          uint32_t c0 = __builtin_amdgcn_perm(a23, a01, 0x05040100u);     // col 0: r0 r1 r2 r3
+          uint32_t c1 = __builtin_amdgcn_perm(a23, a01, 0x07060302u);     // col 1
+          uint32_t c2 = __builtin_amdgcn_perm(b23, b01, 0x05040100u);     // col 2
+          uint32_t c3 = __builtin_amdgcn_perm(b23, b01, 0x07060302u);     // col 3
+          const int cb = 8 * cc + 4 * half;
+          const int di = lr >> 2;
+          tile_t[lds_slot<kColDwords>(cb + 0, di)] = c0;
+          tile_t[lds_slot<kColDwords>(cb + 1, di)] = c1;
+          tile_t[lds_slot<kColDwords>(cb + 2, di)] = c2;
+          tile_t[lds_slot<kColDwords>(cb + 3, di)] = c3;
+        }
       }
     }
   }
@@ -133,8 +181,8 @@ quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t
   if (!want_t) return;
 
   // q_t: each item is 16 consecutive rows of one column (one 16-byte store).
-  constexpr int kChunksPerCol = kQTR / 16;                  // 8
-  constexpr int kItems = kQTC * kChunksPerCol;              // 2048
+  constexpr int kChunksPerCol = kQTR / 16;
+  constexpr int kItems = kQTC * kChunksPerCol;
 #pragma unroll
   for (int it = 0; it < kItems / kQThreads; ++it) {
     const int idx = it * kQThreads + t;
@@ -144,18 +192,39 @@ quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t
     const int64_t gr = row0 + 16 * ch;
     if (gc < cols && gr < rows) {
       uint4 o;
-      o.x = tile_t[lds_slot(c, 4 * ch + 0)];
-      o.y = tile_t[lds_slot(c, 4 * ch + 1)];
-      o.z = tile_t[lds_slot(c, 4 * ch + 2)];
-      o.w = tile_t[lds_slot(c, 4 * ch + 3)];
-      *reinterpret_cast<uint4*>(q_t + gc * rows + gr) = o;
+      o.x = tile_t[lds_slot<kColDwords>(c, 4 * ch + 0)];
+      o.y = tile_t[lds_slot<kColDwords>(c, 4 * ch + 1)];
+      o.z = tile_t[lds_slot<kColDwords>(c, 4 * ch + 2)];
+      o.w = tile_t[lds_slot<kColDwords>(c, 4 * ch + 3)];
+      st16<NT>(q_t + gc * rows + gr, o);
     }
   }
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+template <class QC>
+hipError_t run_q(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_valid,
+                 const float* scale_inv, uint8_t* q, uint8_t* q_t, float* amax, hipStream_t s) {
+  const int64_t tiles_r = (rows + QC::kQTR - 1) / QC::kQTR;
+  const int64_t tiles_c = (cols + QC::kQTC - 1) / QC::kQTC;
+  const int64_t tiles = tiles_r * tiles_c;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_tensorwise_kernel<QC>, dim3((unsigned)tiles), dim3(QC::kQThreads), 0,
+                     s, x, rows, cols, rows_valid, scale_inv, q, q_t,
+                     reinterpret_cast<uint32_t*>(amax), tiles_c);
+  return hipGetLastError();
+}
+
+int quant_cfg() {
+  static int v = [] {
+    const char* e = getenv("FP8LIN_QUANT_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
 }
 
 }  // namespace
@@ -163,6 +232,7 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
+  if (blocks > 65535) blocks = 65535;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
   return hipGetLastError();
 }
@@ -170,20 +240,38 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t rows, int64_t cols,
                                       int64_t rows_valid, const float* scale_inv, uint8_t* q,
                                       uint8_t* q_t, float* amax, hipStream_t s) {
+  hipError_t e = hipSuccess;
   if (amax != nullptr) {
-    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 0u, 1, s);
+    e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 0u, 1, s);
     if (e != hipSuccess) return e;
   }
   if (rows == 0 || cols == 0) return hipSuccess;
   if (q == nullptr && q_t == nullptr && amax == nullptr) return hipSuccess;
-  const int64_t tiles_r = (rows + kQTR - 1) / kQTR;
-  const int64_t tiles_c = (cols + kQTC - 1) / kQTC;
-  const int64_t tiles = tiles_r * tiles_c;
-  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quantize_tensorwise_kernel, dim3((unsigned)tiles), dim3(kQThreads), 0, s,
-                     x, rows, cols, rows_valid, scale_inv, q, q_t,
-                     reinterpret_cast<uint32_t*>(amax), tiles_c);
-  return hipGetLastError();
+  if (rows_valid == 0) {
+    // nothing to read: every code is 0x00 (amax was set to 0 above)
+    // (a fill kernel, not a memset: the call may be captured in a graph)
+    if (q != nullptr &&
+        (e = launch_fill_u32(reinterpret_cast<uint32_t*>(q), 0u, rows * cols / 4, s)) != hipSuccess)
+      return e;
+    if (q_t != nullptr &&
+        (e = launch_fill_u32(reinterpret_cast<uint32_t*>(q_t), 0u, rows * cols / 4, s)) != hipSuccess)
+      return e;
+    return hipSuccess;
+  }
+  switch (quant_cfg()) {
+    case 1: return run_q<QCfg<128, 256, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 2: return run_q<QCfg<64, 512, 256, true>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 3: return run_q<QCfg<64, 512, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 4: return run_q<QCfg<128, 512, 512, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 5: return run_q<QCfg<64, 256, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 6: return run_q<QCfg<128, 128, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 7: return run_q<QCfg<256, 256, 512, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 8: return run_q<QCfg<256, 512, 1024, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 9: return run_q<QCfg<128, 512, 512, true>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 10: return run_q<QCfg<256, 256, 512, true>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 11: return run_q<QCfg<256, 128, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    default: return run_q<QCfg<128, 256, 256, true>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+  }
 }
 
 }  // namespace fp8lin
