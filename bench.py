@@ -40,6 +40,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the block-recipe and packed-varlen measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 512 MiB buffer three times (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -141,6 +143,115 @@ def cpu_baseline(sample_tokens: int) -> dict:
                        f"float64 via BLAS with {blas_threads} threads) + quantize of {R} of {N} "
                        f"weight rows (single-threaded numpy), scaled linearly to the 3-linear step; "
                        f"measured {t_w + t_q + t_g:.1f} s, extrapolated step {t_step:.1f} s")}
+
+
+def _time_steps(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure_block_recipe(torch, m, workloads, steps, warmup):
+    """Block recipe (1x128 activation/gradient tiles, 128x128 weight tiles, current
+    scaling) at M=16384, K=N=8192: quantize x, W, g and the three GEMMs per step."""
+    M, K, N = 16384, 8192, 8192
+    d = workloads.linear_inputs(5, 0)
+    dev = torch.device("cuda:0")
+
+    def up(b):
+        return torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w, g = up(d["x"]), up(d["w"]), up(d["g"])
+    del d
+    B, W128 = m.FP8_BLOCK_1x128, m.FP8_BLOCK_128x128
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    buf = dict(qx=torch.empty((M, K), **u8), qxt=torch.empty((K, M), **u8),
+               sx=torch.empty((M, K // 128), **f32), sxt=torch.empty((K, M // 128), **f32),
+               qw=torch.empty((N, K), **u8), qwt=torch.empty((K, N), **u8),
+               sw=torch.empty((N // 128, K // 128), **f32), swt=torch.empty((K // 128, N // 128), **f32),
+               qg=torch.empty((M, N), **u8), qgt=torch.empty((N, M), **u8),
+               sg=torch.empty((M, N // 128), **f32), sgt=torch.empty((N, M // 128), **f32),
+               y=torch.empty((M, N), **bf), dx=torch.empty((M, K), **bf), dw=torch.empty((N, K), **bf))
+    gemm_ev, q_ev = [], []
+
+    def ev(lst, fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        lst.append((a, b))
+
+    def step():
+        b = buf
+        ev(q_ev, lambda: m.fp8_quantize_amax(x, gran=B, q=b["qx"], q_t=b["qxt"], scale=b["sx"],
+                                             scale_t=b["sxt"], want_amax=False))
+        ev(q_ev, lambda: m.fp8_quantize_amax(w, gran=W128, q=b["qw"], q_t=b["qwt"], scale=b["sw"],
+                                             scale_t=b["swt"], want_amax=False))
+        ev(q_ev, lambda: m.fp8_quantize_amax(g, gran=B, q=b["qg"], q_t=b["qgt"], scale=b["sg"],
+                                             scale_t=b["sgt"], want_amax=False))
+        ev(gemm_ev, lambda: m.fp8_linear_fwd(b["qx"], b["qw"], b["sx"], b["sw"], y=b["y"], gran=B))
+        ev(gemm_ev, lambda: m.fp8_linear_dgrad(b["qg"], b["qwt"], b["sg"], b["swt"], dx=b["dx"],
+                                               gran=B))
+        ev(gemm_ev, lambda: m.fp8_linear_wgrad(b["qgt"], b["qxt"], b["sgt"], b["sxt"], dw=b["dw"],
+                                               gran=B))
+
+    ms = _time_steps(torch, step, steps, warmup)
+    gemm_ev, q_ev = gemm_ev[-3 * steps:], q_ev[-3 * steps:]
+    g_ms = [a.elapsed_time(b) for a, b in gemm_ev]
+    q_ms = [a.elapsed_time(b) for a, b in q_ev]
+    flops = 6.0 * M * N * K
+    q_bytes = 4 * (M * K + N * K + M * N)        # bf16 in, codes + transposed codes out
+    return {"workload": "block recipe linear fwd+dgrad+wgrad, M=16384 K=N=8192, N(0,1) with 1% x100",
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "ms_per_step": round(ms, 4),
+            "gemm_tflops_per_launch": round(2.0 * M * N * K / (np.mean(g_ms) * 1e-3) / 1e12, 1),
+            "gemm_frac_of_fp8_peak": round(2.0 * M * N * K / (np.mean(g_ms) * 1e-3) / 1e12
+                                           / PEAK_FP8_TFLOPS, 4),
+            "quantize_gbs": round(q_bytes / (np.sum(q_ms) / steps * 1e-3) / 1e9, 1),
+            "quantize_frac_of_hbm_peak": round(q_bytes / (np.sum(q_ms) / steps * 1e-3) / 1e9
+                                               / PEAK_HBM_GBS, 4)}
+
+
+def measure_varlen(torch, m, workloads, steps, warmup):
+    """Packed varlen batch: 64 sequences of U{32..2048} tokens, padded to a multiple of 16,
+    K = N = 4096, one linear fwd+bwd with delayed scaling and rows_valid = T."""
+    d = workloads.varlen_batch(4)
+    T = d["T"]
+    dev = torch.device("cuda:0")
+
+    def up(b):
+        return torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w, g = up(d["x"]), up(d["w"]), up(d["g"])
+    del d
+    _, T_pad = m.fp8_pad_tokens(x, query_only=True)
+    xp = torch.empty((T_pad, x.shape[1]), dtype=x.dtype, device=dev)
+    gp = torch.empty((T_pad, g.shape[1]), dtype=g.dtype, device=dev)
+    lin = m.DelayedScalingLinear(dev)
+
+    def step():
+        m.fp8_pad_tokens(x, x_pad=xp)
+        m.fp8_pad_tokens(g, x_pad=gp)
+        lin.begin_step()
+        lin.forward(xp, w, rows_valid=T)
+        lin.backward(gp)
+        lin.end_step()
+
+    ms = _time_steps(torch, step, steps, warmup)
+    flops = 6.0 * T_pad * 4096 * 4096
+    return {"workload": "packed THD batch, 64 seqs U{32..2048}, K=N=4096, delayed scaling",
+            "tokens": T, "tokens_padded": T_pad, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "ms_per_step": round(ms, 4)}
 
 
 def main():
@@ -263,6 +374,13 @@ def main():
         "wall_s_timed": round(wall_s, 3),
         "device": torch.cuda.get_device_name(0),
     }
+    del t, bufs, outs, lins
+    if not args.headline_only:
+        torch.cuda.empty_cache()
+        line["other_rows"] = {
+            "block_recipe": measure_block_recipe(torch, m, workloads, max(3, args.steps // 3), 2),
+            "packed_varlen_padding": measure_varlen(torch, m, workloads, max(3, args.steps // 3), 2),
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
     else:

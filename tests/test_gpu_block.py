@@ -84,3 +84,69 @@ def test_block_linear_step(lib, M, K, N, rv):
     assert_within(host_bf16_f64(dx), r["dx"], db, "block dgrad")
     wb = block.block_error_bound(r["qg_t"], r["qx_t"], r["sg_t"], r["sx_t"], 1)
     assert_within(host_bf16_f64(dw), r["dw"], wb, "block wgrad")
+
+
+def test_block_full_size_sampled(lib):
+    """The block recipe at its benchmark size (M=16384, K=N=8192, outliers x100 at 1%):
+    tile grids bit-exact on sampled tiles, GEMM outputs on sampled elements."""
+    M, K, N = 16384, 8192, 8192
+    d = workloads.linear_inputs(5, 0)
+    x, w, g = d["x"], d["w"], d["g"]
+    assert x.shape == (M, K) and w.shape == (N, K) and g.shape == (M, N)
+    B = lib.FP8_BLOCK_1x128
+    note("block full size: quantize x, w, g")
+    qx, qx_t, _, sx, sx_t = lib.fp8_quantize_amax(dev_bf16(x), gran=B)
+    qw, qw_t, _, sw, sw_t = lib.fp8_quantize_amax(dev_bf16(w), gran=lib.FP8_BLOCK_128x128)
+    qg, qg_t, _, sg, sg_t = lib.fp8_quantize_amax(dev_bf16(g), gran=B)
+    note("block full size: fwd, dgrad, wgrad")
+    y = lib.fp8_linear_fwd(qx, qw, sx, sw, gran=B)
+    dx = lib.fp8_linear_dgrad(qg, qw_t, sg, sw_t, gran=B)
+    dw = lib.fp8_linear_wgrad(qg_t, qx_t, sg_t, sx_t, gran=B)
+    torch.cuda.synchronize()
+    yh, dxh, dwh = host_bf16_f64(y), host_bf16_f64(dx), host_bf16_f64(dw)
+    sxh, swh, sgh = sx.cpu().numpy(), sw.cpu().numpy(), sg.cpu().numpy()
+    sx_th, sg_th = sx_t.cpu().numpy(), sg_t.cpu().numpy()
+    qxh, qwh, qgh = host_u8(qx), host_u8(qw), host_u8(qg)
+    rng = np.random.default_rng(12)
+    # tile grids: rows of x (1x128 tiles), one 128x128 block row of W, columns of x (the
+    # transposed copy's tiles along tokens); the oracle quantizes the 128-row / 128-column
+    # slab that holds each sample
+    for r in rng.choice(M, 3, replace=False):
+        r0 = int(r) - int(r) % 128
+        oq, _, _, os_, _ = block.quantize_1x128(np.ascontiguousarray(x[r0:r0 + 128]))
+        assert_same_bytes(qxh[r], oq[r % 128], f"qx row {r}")
+        _f32_equal(sxh[r], os_[r % 128], f"sx row {r}")
+    wq, _, _, wsc, _ = block.quantize_128x128(np.ascontiguousarray(w[:128]))
+    assert_same_bytes(qwh[:128], wq, "qw block row 0")
+    _f32_equal(swh[:1], wsc, "sw block row 0")
+    qx_th = host_u8(qx_t)
+    for c in rng.choice(K, 2, replace=False):
+        c0 = int(c) - int(c) % 128
+        _, oqt, _, _, ost = block.quantize_1x128(np.ascontiguousarray(x[:, c0:c0 + 128]))
+        assert_same_bytes(qx_th[c], oqt[c % 128], f"qx_t row {c}")
+        _f32_equal(sx_th[c], ost[c % 128], f"sx_t row {c}")
+    # GEMM samples: exact per-block sums from the GPU's own codes and scales (checked above)
+    for _ in range(24):
+        m, n, k = int(rng.integers(0, M)), int(rng.integers(0, N)), int(rng.integers(0, K))
+        ex = block.block_scaled_gemm(qxh[m:m + 1], qwh[n:n + 1], sxh[m:m + 1],
+                                     swh[n // 128:n // 128 + 1], 1)
+        bd = block.block_error_bound(qxh[m:m + 1], qwh[n:n + 1], sxh[m:m + 1],
+                                     swh[n // 128:n // 128 + 1], 1)
+        assert abs(yh[m, n] - ex[0, 0]) <= bd[0, 0], ("y", m, n)
+    qw_th = host_u8(qw_t)
+    sw_th = sw_t.cpu().numpy()
+    for _ in range(12):
+        m, k = int(rng.integers(0, M)), int(rng.integers(0, K))
+        ex = block.block_scaled_gemm(qgh[m:m + 1], qw_th[k:k + 1], sgh[m:m + 1],
+                                     sw_th[k // 128:k // 128 + 1], 1)
+        bd = block.block_error_bound(qgh[m:m + 1], qw_th[k:k + 1], sgh[m:m + 1],
+                                     sw_th[k // 128:k // 128 + 1], 1)
+        assert abs(dxh[m, k] - ex[0, 0]) <= bd[0, 0], ("dx", m, k)
+    qg_th = host_u8(qg_t)
+    for _ in range(12):
+        n, k = int(rng.integers(0, N)), int(rng.integers(0, K))
+        ex = block.block_scaled_gemm(qg_th[n:n + 1], qx_th[k:k + 1], sg_th[n:n + 1],
+                                     sx_th[k:k + 1], 1)
+        bd = block.block_error_bound(qg_th[n:n + 1], qx_th[k:k + 1], sg_th[n:n + 1],
+                                     sx_th[k:k + 1], 1)
+        assert abs(dwh[n, k] - ex[0, 0]) <= bd[0, 0], ("dw", n, k)
