@@ -39,7 +39,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the block-recipe and packed-varlen measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -59,6 +59,40 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read_per_copy": nbytes,
                                            "bytes_written_per_copy": nbytes, "copies": 3}}))
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mlp_8192x4096x14336.txt")
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, scaled by the copy calibration; None when the summary is missing or the kernel's
+    sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    for block in text.split("\n\n"):
+        kv = {}
+        for ln in block.splitlines():
+            if ln and not ln.startswith("#"):
+                k, _, v = ln.partition(" ")
+                kv[k] = v.strip()
+        if kv.get("kernel") != kernel:
+            continue
+        h = hashlib.sha256()
+        for f in kv["sources"].split():
+            try:
+                h.update(open(os.path.join(ROOT, f), "rb").read())
+            except OSError:
+                return None
+        if h.hexdigest()[:16] != kv["source_sha256"]:
+            return None
+        rd = float(kv["fetch_kib_mean"]) * float(kv["fetch_factor"]) * 1024
+        wr = float(kv["write_kib_mean"]) * float(kv["write_factor"]) * 1024
+        return {"bytes": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr)}
+    return None
 
 
 class EventProbe:
@@ -341,6 +375,8 @@ def main():
     q_bytes_step = 4 * q_elems_step                # 2 B read + 1 B Q + 1 B Q^T per element
     q_ms_step = float(np.sum(q_ms)) / args.steps
     q_gbs = q_bytes_step / (q_ms_step * 1e-3) / 1e9
+    g_traffic = counter_traffic("gemm_fp8_persist_kernel")
+    q_traffic = counter_traffic("quantize_tensorwise_kernel")
     line = {
         "metric": "fp8 linear fwd+bwd TFLOP/s at 8192x4096x14336; quantize+amax GB/s",
         "value": round(value, 2),
@@ -357,15 +393,21 @@ def main():
         "config": {"workload": "Llama-8B-shaped MLP block fwd+bwd (gate, up: 4096->14336; "
                                "down: 14336->4096), delayed tensorwise scaling",
                    "tokens": M, "K": K, "N": N, "linears": 3, "flops_per_step": flops_step},
-        "roofline": {"bound": "mfma", "kernel": "gemm_fp8_kernel",
+        "roofline": {"bound": "mfma", "kernel": "gemm_fp8_persist_kernel",
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None, "avg_launch_us": round(gemm_avg * 1e3, 2),
+                     "traffic": g_traffic and g_traffic["bytes"],
+                     "traffic_detail": g_traffic,
+                     # A + B codes (1 B) in, D (bf16) out, averaged over fwd / dgrad / wgrad
+                     "algorithmic_bytes_per_launch": 4 * (M * K + N * K + M * N) // 3,
+                     "avg_launch_us": round(gemm_avg * 1e3, 2),
                      "launches": len(gemm_ms)},
         "quantize_amax": {"achieved": round(q_gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
                           "frac": round(q_gbs / PEAK_HBM_GBS, 4),
                           "avg_launch_us": round(float(np.mean(q_ms)) * 1e3, 2),
-                          "bytes_per_step": q_bytes_step},
+                          "bytes_per_step": q_bytes_step,
+                          "traffic": q_traffic and q_traffic["bytes"],
+                          "algorithmic_bytes_per_launch": q_bytes_step // 9},
         "breakdown_ms_per_step": {"gemm": round(float(np.sum(gemm_ms)) / args.steps, 4),
                                   "quantize": round(q_ms_step, 4),
                                   "scale_update": round(float(np.sum(s_ms)) / args.steps, 4)},
