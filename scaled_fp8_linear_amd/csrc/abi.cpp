@@ -57,8 +57,9 @@ int check_gemm(const char* fn, const void* a, const void* b, const float* s1, co
   if (gran == FP8_BLOCK_1x128 && kc % 128)
     return fail(FP8_ERR_SHAPE, "%s: block recipe needs the contraction size %% 128 == 0 (got %lld)",
                 fn, (long long)kc);
-  if (rows_a * kc >= kMaxOperandBytes || rows_b * kc >= kMaxOperandBytes)
-    return fail(FP8_ERR_UNSUPPORTED, "%s: an operand holds 2^31 bytes or more", fn);
+  if (rows_a * kc >= kMaxOperandBytes || rows_b * kc >= kMaxOperandBytes ||
+      rows_a * rows_b * 2 >= kMaxOperandBytes)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: an operand or the output holds 2^31 bytes or more", fn);
   if (kc >= kMaxContraction)
     return fail(FP8_ERR_UNSUPPORTED, "%s: contraction size %lld >= 2^17", fn, (long long)kc);
   if (rows_a * rows_b > 0) {

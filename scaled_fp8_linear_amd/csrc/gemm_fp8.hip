@@ -85,6 +85,12 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
 }
 
 template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // this wave's loads older than the newest N have landed
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int N>
 __device__ __forceinline__ void wait_vm_lgkm() {
   // this wave's loads older than the newest N have landed; its LDS reads are done
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
@@ -138,9 +144,10 @@ struct Tile {
   uint16_t* D;
   int M, N, K, M_valid, nk;
   v4i rsA, rsB;
+  __amdgpu_buffer_rsrc_t rsD;   // D as a raw buffer: stores at offsets past its end are dropped
   int wave, wm, wn, fr, fg, ch, r0, c_lo, c_hi;
   uint32_t step_rows;
-  float s_tensor;   // tensorwise: sa * sb
+  float s_tensor;   // tensorwise: sa * sb (wave-uniform)
 
   v16f acc[C::TM][C::TN];
   v16f part[C::BLOCK ? C::TM : 1][C::BLOCK ? C::TN : 1];
@@ -155,6 +162,7 @@ struct Tile {
     nk = (K + kBKS - 1) / kBKS;
     rsA = make_rsrc(A, (uint32_t)(M * K));
     rsB = make_rsrc(B, (uint32_t)(N * K));
+    rsD = __builtin_amdgcn_make_buffer_rsrc(D_, 0, M * N * 2, kRsrcWord3);
     const int t = threadIdx.x, lane = t & 63;
     wave = __builtin_amdgcn_readfirstlane(t >> 6);
     wm = wave / C::WN;
@@ -172,7 +180,9 @@ struct Tile {
     // [32 fg, 32 fg + 32) of row fr, i.e. chunks 2 fg and 2 fg + 1
     c_lo = swz64<C::SWZ>(fr, 2 * fg) * 16;
     c_hi = swz64<C::SWZ>(fr, 2 * fg + 1) * 16;
-    s_tensor = C::BLOCK ? 1.0f : sa[0] * sb[0];
+    s_tensor = C::BLOCK ? 1.0f
+                        : __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                        __builtin_bit_cast(int, sa[0] * sb[0])));
     zero_acc();
   }
 
@@ -216,6 +226,30 @@ struct Tile {
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
     return v;
+  }
+
+  // operand fragments of one K step: the wave's TM A tiles and TN B tiles
+  struct Frags { v8i a[C::TM]; v8i b[C::TN]; };
+
+  __device__ void read_frags(Frags& F, const uint8_t* stage) const {
+    const uint8_t* pA = stage + (wm * C::WTM + fr) * kBKS;
+    const uint8_t* pB = stage + C::BM * kBKS + (wn * C::WTN + fr) * kBKS;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) F.b[j] = frag(pB, 32 * j);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) F.a[i] = frag(pA, 32 * i);
+  }
+
+  // FIRST: the tile's first K step, which starts the sums from zero
+  template <bool FIRST>
+  __device__ void mma(const Frags& F) {
+    const v16f z = {};
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            F.b[j], F.a[i], FIRST ? z : acc[i][j], 0, 0, 0, 0, 0, 0);
   }
 
   // block recipe: load the scales of 128-wide K block kb of the tile at (m0, n0)
@@ -282,7 +316,9 @@ struct Tile {
     }
   }
 
-  // write the tile at (m0, n0): scale, round to bf16, 16 bytes per lane
+  // write the tile at (m0, n0): scale, round to bf16, 16 bytes per lane. Every lane
+  // issues exactly 2 TM TN buffer stores; pieces outside D get an offset past its end,
+  // which the buffer range check drops.
   __device__ void epilogue(int m0, int n0) {
     const float s = s_tensor;
 #pragma unroll
@@ -304,11 +340,11 @@ struct Tile {
           const auto w0 = __builtin_amdgcn_permlane32_swap(q[0][0], q[1][0], false, false);
           const auto w1 = __builtin_amdgcn_permlane32_swap(q[0][1], q[1][1], false, false);
           const int n = n0 + wn * C::WTN + 32 * j + 8 * (2 * p + fg);
-          if (m < M && n < N) {
-            uint4 o = make_uint4(w0[0], w1[0], w0[1], w1[1]);
-            if (!live) o = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(D + (int64_t)m * N + n) = o;
-          }
+          v4i o = {(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
+          if (!live) o = v4i{0, 0, 0, 0};
+          const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u
+                                                : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
         }
       }
     }
@@ -415,6 +451,326 @@ gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict
     next_tb = tile_base(ti + 2);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may land after exit
+}
+
+// ---------------------------------------------------------------------------
+// Persistent kernel with register-level fragment pipelining (tensorwise scaling).
+// Each wave keeps two fragment sets: while the MFMAs of K step j consume one, the
+// LDS reads of step j + 1 fill the other, interleaved one for one, so the matrix
+// cores and the LDS work at the same time.
+// LDS ring of STAGES slots, indexed at run time. At the top of step j a wave waits
+// for its own loads of step j + 1, and one barrier publishes that slot; the same
+// barrier frees the slot of step j - 1, whose fragments every wave has already fed
+// to the MFMAs of step j - 1, and that slot is refilled with step j + STAGES - 1.
+// So the barrier never waits on the LDS reads just issued for the next step.
+// A tile's bf16 stores (exactly 2 TM TN buffer stores per lane, in range or not) enter
+// the same in-order memory counter as the loads; for the first STAGES - 2 steps of the
+// next tile the waits allow them to stay in flight.
+template <class C>
+__global__ void __launch_bounds__(C::kThreads, 1)
+gemm_fp8_fpipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                      const float* __restrict__ sa, const float* __restrict__ sb,
+                      uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
+                      int tiles_n, int split_m, int split_n) {
+  static_assert(!C::BLOCK, "tensorwise only");
+  static_assert(C::STAGES >= 4, "two slots ahead of the refill");
+  constexpr int SB = C::kStageBytes;
+  constexpr int kStores = 2 * C::TM * C::TN;            // epilogue stores per lane
+  constexpr int kWaitN = C::kLoadsPerStage * (C::STAGES - 3);
+  static_assert(kWaitN + kStores <= 63, "vmcnt range");
+  constexpr int kDsReads = 2 * (C::TM + C::TN);
+  constexpr int kMfma = C::TM * C::TN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::STAGES * SB];
+
+  Tile<C> T;
+  T.init(A, B, sa, sb, D, M, N, K, M_valid);
+
+  // tile assignment: as in gemm_fp8_persist_kernel (one rectangle of tiles per XCD)
+  const int nwg = gridDim.x;
+  int bm0 = 0, bn0 = 0, bmc = tiles_m, bnc = tiles_n, slot = blockIdx.x, nslots = nwg;
+  if (split_m > 0) {
+    const int xcd = blockIdx.x & 7;
+    const int rm = (tiles_m + split_m - 1) / split_m, rn = (tiles_n + split_n - 1) / split_n;
+    const int bx = xcd / split_n, by = xcd % split_n;
+    bm0 = bx * rm;
+    bn0 = by * rn;
+    bmc = max(0, min(tiles_m, bm0 + rm) - bm0);
+    bnc = max(0, min(tiles_n, bn0 + rn) - bn0);
+    slot = blockIdx.x >> 3;
+    nslots = nwg >> 3;
+  }
+  const int block_tiles = bmc * bnc;
+  const int count = slot < block_tiles ? (block_tiles - slot + nslots - 1) / nslots : 0;
+  auto tile_mn = [&](int ti, int& m0, int& n0) {
+    const int lid = slot + ti * nslots;
+    const int per_group = C::GROUP_M * bnc;
+    const int group = lid / per_group;
+    const int first_m = group * C::GROUP_M;
+    const int gsize = min(bmc - first_m, C::GROUP_M);
+    const int in_group = lid - group * per_group;
+    m0 = (bm0 + first_m + in_group % gsize) * C::BM;
+    n0 = (bn0 + in_group / gsize) * C::BN;
+  };
+  auto tile_base = [&](int ti) {
+    int m0 = 0, n0 = 0;
+    if (ti < count) tile_mn(ti, m0, n0);
+    return T.base(ti < count, m0, n0);
+  };
+
+  const int nk = T.nk;                 // even and >= STAGES (the host checks)
+  auto cur_tb = tile_base(0), next_tb = tile_base(1);
+  typename Tile<C>::Frags F0, F1;
+  int rd = 1, wr = C::STAGES - 1;      // slots of steps j + 1 and j - 1 (mod STAGES)
+
+  // One K step. FIRST: the tile's first step (sums start at zero). READ: fetch the next
+  // step's fragments (not at the tile's last step: they are fetched after the epilogue,
+  // so that they do not hold registers through it).
+  auto step = [&](auto FIRST_, auto READ_, typename Tile<C>::Frags& Fc,
+                  typename Tile<C>::Frags& Fn, int kk, bool loose) {
+    constexpr bool FIRST = decltype(FIRST_)::value != 0, READ = decltype(READ_)::value != 0;
+#ifndef FP8LIN_FPIPE_LOOSE
+#define FP8LIN_FPIPE_LOOSE 1
+#endif
+    if (FP8LIN_FPIPE_LOOSE && loose) wait_vm<kWaitN + kStores>();
+    else wait_vm<kWaitN>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int kr = kk + C::STAGES - 1;                  // K step that refills slot wr
+    if (kr < nk) T.issue(smem + wr * SB, cur_tb, kr);
+    else T.issue(smem + wr * SB, next_tb, kr - nk);
+    if constexpr (READ) T.read_frags(Fn, smem + rd * SB);
+    T.template mma<FIRST>(Fc);
+    if constexpr (READ) {
+#pragma unroll
+      for (int x = 0; x < kMfma; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
+        if (x < kDsReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+    }
+    rd = rd + 1 == C::STAGES ? 0 : rd + 1;
+    wr = wr + 1 == C::STAGES ? 0 : wr + 1;
+  };
+
+#pragma unroll
+  for (int i = 0; i < C::STAGES - 1; ++i) T.issue(smem + i * SB, cur_tb, i);
+  wait_vm<C::kLoadsPerStage * (C::STAGES - 2)>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  T.read_frags(F0, smem);
+  for (int ti = 0; ti < count; ++ti) {
+    int cm0, cn0;
+    tile_mn(ti, cm0, cn0);
+    const bool after = ti > 0;   // the previous tile's stores may still be in flight
+    // steps 0, 1 | 2 .. nk - 3 | nk - 2, nk - 1 (nk is even and at least 6)
+    step(IC<1>{}, IC<1>{}, F0, F1, 0, after);
+    step(IC<0>{}, IC<1>{}, F1, F0, 1, after && 1 <= C::STAGES - 3);
+    for (int kk = 2; kk < nk - 2; kk += 2) {
+      step(IC<0>{}, IC<1>{}, F0, F1, kk, after && kk <= C::STAGES - 3);
+      step(IC<0>{}, IC<1>{}, F1, F0, kk + 1, after && kk + 1 <= C::STAGES - 3);
+    }
+    step(IC<0>{}, IC<1>{}, F0, F1, nk - 2, false);
+    step(IC<0>{}, IC<0>{}, F1, F0, nk - 1, false);
+    T.epilogue(cm0, cn0);
+    // the next tile's first fragments (K step nk, one slot behind rd, which has already
+    // moved on to step nk + 1); the barrier of step nk - 1 published that slot
+    T.read_frags(F0, smem + (rd == 0 ? C::STAGES - 1 : rd - 1) * SB);
+    cur_tb = next_tb;
+    next_tb = tile_base(ti + 2);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // no load may land after exit
+}
+
+// ---------------------------------------------------------------------------
+// Wide-stage persistent kernel (tensorwise scaling), 256x256 tiles, 4 waves.
+// An LDS stage holds 128 K bytes of the tile's 256 A rows and 256 B rows (64 KB), so
+// every global load brings a whole 128-byte line per row: a 64-byte step would fetch
+// each line in two halves, one step apart, which halves the L2 -> CU throughput.
+// Two LDS slots. Stage s + 1 waits in VGPRs (one 16-byte buffer load per lane and
+// 32 rows) while stage s is multiplied, is written to the free slot at the start of
+// stage s, and the loads of stage s + 2 go out right after; they have two MFMA steps
+// to land. One barrier per stage, in its middle: it publishes stage s + 1 and, as
+// every wave has finished its LDS reads of stage s - 1 before it, frees that slot. Within a stage, the two 64-byte MFMA steps are fragment-pipelined as in
+// gemm_fp8_fpipe_kernel. LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled
+// by (row / 2) % 8, which keeps both the row-wise writes and the fragment reads free
+// of bank conflicts. The loads go through the compiler, which places their waits.
+constexpr int kStageK = 128;
+
+template <class C>
+__global__ void __launch_bounds__(C::kThreads, 1)
+gemm_fp8_wide_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                     const float* __restrict__ sa, const float* __restrict__ sb,
+                     uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
+                     int tiles_n, int split_m, int split_n) {
+  static_assert(!C::BLOCK, "tensorwise only");
+  constexpr int SB = (C::BM + C::BN) * kStageK;
+  constexpr int kPassRows = C::kThreads / 8;                 // rows per load pass
+  constexpr int kPassA = C::BM / kPassRows, kPassB = C::BN / kPassRows;
+  constexpr int kLoads = kPassA + kPassB;
+  constexpr int kDsReads = 2 * (C::TM + C::TN);
+  constexpr int kMfma = C::TM * C::TN;
+  static_assert(C::BM % kPassRows == 0 && C::BN % kPassRows == 0, "load passes");
+  // two slots as two arrays, so that the compiler sees that the reads of one and the
+  // writes of the other never alias (and can interleave them)
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[SB];
+
+  Tile<C> T;
+  T.init(A, B, sa, sb, D, M, N, K, M_valid);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, M * K, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, N * K, kRsrcWord3);
+
+  // tile assignment: as in gemm_fp8_persist_kernel (one rectangle of tiles per XCD)
+  const int nwg = gridDim.x;
+  int bm0 = 0, bn0 = 0, bmc = tiles_m, bnc = tiles_n, slot = blockIdx.x, nslots = nwg;
+  if (split_m > 0) {
+    const int xcd = blockIdx.x & 7;
+    const int rm = (tiles_m + split_m - 1) / split_m, rn = (tiles_n + split_n - 1) / split_n;
+    const int bx = xcd / split_n, by = xcd % split_n;
+    bm0 = bx * rm;
+    bn0 = by * rn;
+    bmc = max(0, min(tiles_m, bm0 + rm) - bm0);
+    bnc = max(0, min(tiles_n, bn0 + rn) - bn0);
+    slot = blockIdx.x >> 3;
+    nslots = nwg >> 3;
+  }
+  const int block_tiles = bmc * bnc;
+  const int count = slot < block_tiles ? (block_tiles - slot + nslots - 1) / nslots : 0;
+  auto tile_mn = [&](int ti, int& m0, int& n0) {
+    const int lid = slot + ti * nslots;
+    const int per_group = C::GROUP_M * bnc;
+    const int group = lid / per_group;
+    const int first_m = group * C::GROUP_M;
+    const int gsize = min(bmc - first_m, C::GROUP_M);
+    const int in_group = lid - group * per_group;
+    m0 = (bm0 + first_m + in_group % gsize) * C::BM;
+    n0 = (bn0 + in_group / gsize) * C::BN;
+  };
+
+  // load plan: lane t takes 16-byte chunk t % 8 of rows t / 8 + 32 i
+  const int t = threadIdx.x;
+  const int lrow = t >> 3, lch = t & 7;
+  const uint32_t st_off = (uint32_t)(lrow * kStageK + 16 * (lch ^ ((lrow >> 1) & 7)));
+  struct Rows { uint32_t a, b; };     // byte offsets of this lane's first rows, K block 0
+  auto rows_of = [&](int ti) -> Rows {
+    if (ti >= count) return {kOutOfRange, kOutOfRange};
+    int m0, n0;
+    tile_mn(ti, m0, n0);
+    return {(uint32_t)(m0 + lrow) * (uint32_t)K + 16u * lch,
+            (uint32_t)(n0 + lrow) * (uint32_t)K + 16u * lch};
+  };
+  const uint32_t pass_step = (uint32_t)kPassRows * (uint32_t)K;
+  using u4 = decltype(__builtin_amdgcn_raw_buffer_load_b128(rA, 0, 0, 0));
+  u4 buf[kLoads];
+  auto gload = [&](Rows r, int kb) {
+    const bool ok = r.a != kOutOfRange;
+    const uint32_t k0 = (uint32_t)kb * kStageK;
+#pragma unroll
+    for (int i = 0; i < kPassA; ++i)
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, ok ? r.a + i * pass_step + k0 : kOutOfRange,
+                                                     0, 0);
+#pragma unroll
+    for (int i = 0; i < kPassB; ++i)
+      buf[kPassA + i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rB, ok ? r.b + i * pass_step + k0 : kOutOfRange, 0, 0);
+  };
+  auto swrite = [&](uint8_t* slot_mem) {
+    uint8_t* base = slot_mem + st_off;
+#pragma unroll
+    for (int i = 0; i < kPassA; ++i)
+      *reinterpret_cast<u4*>(base + i * kPassRows * kStageK) = buf[i];
+#pragma unroll
+    for (int i = 0; i < kPassB; ++i)
+      *reinterpret_cast<u4*>(base + C::BM * kStageK + i * kPassRows * kStageK) = buf[kPassA + i];
+  };
+  // fragment reads: lane (fr, fg) takes logical chunks 4 h + 2 fg and 4 h + 2 fg + 1 of
+  // its row for MFMA step h of the stage; rows 32 apart share the swizzle
+  const int sw = (T.fr >> 1) & 7;
+  const uint32_t fo00 = T.fr * kStageK + 16 * ((2 * T.fg) ^ sw);
+  const uint32_t fo01 = T.fr * kStageK + 16 * ((2 * T.fg + 1) ^ sw);
+  const uint32_t fo10 = T.fr * kStageK + 16 * ((4 + 2 * T.fg) ^ sw);
+  const uint32_t fo11 = T.fr * kStageK + 16 * ((4 + 2 * T.fg + 1) ^ sw);
+  auto rfrag = [&](typename Tile<C>::Frags& F, const uint8_t* slot_mem, int h) {
+    const uint8_t* pa = slot_mem + (T.wm * C::WTM) * kStageK;
+    const uint8_t* pb = slot_mem + (C::BM + T.wn * C::WTN) * kStageK;
+    const uint32_t o0 = h ? fo10 : fo00, o1 = h ? fo11 : fo01;
+    auto rd = [&](const uint8_t* p) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(p + o0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(p + o1);
+      v8i v;
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      return v;
+    };
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) F.b[j] = rd(pb + 32 * j * kStageK);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) F.a[i] = rd(pa + 32 * i * kStageK);
+  };
+
+  const int ns = K / kStageK;          // stages per tile: even and >= 4 (the host checks)
+  Rows cur = rows_of(0), nxt = rows_of(1);
+  typename Tile<C>::Frags F0, F1;
+
+  // One stage (two MFMA steps) on slot `mine`, the other slot being `other`. Tiles have
+  // an even number of stages, so stage s of every tile uses slot s % 2. FIRST: the
+  // tile's first stage. LAST: its last stage, whose second step fetches no fragments
+  // (the next tile's come after the epilogue).
+  auto stage = [&](auto FIRST_, auto LAST_, int s, uint8_t* mine, uint8_t* other) {
+    constexpr bool FIRST = decltype(FIRST_)::value != 0, LAST = decltype(LAST_)::value != 0;
+    // step h = 0. `other` is already free: its last reads (the previous stage's second
+    // half) were issued before the previous stage's barrier, which each wave passed only
+    // after all of its LDS operations had completed.
+    rfrag(F1, mine, 1);
+    swrite(other);                     // stage s + 1 (loaded during stage s - 1)
+    const int g = s + 2;               // stage to load now: of this tile or of the next
+    gload(g < ns ? cur : nxt, g < ns ? g : g - ns);
+    T.template mma<FIRST>(F0);
+#pragma unroll
+    for (int x = 0; x < kMfma; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+      if (x < kDsReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+      if (x < kLoads) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // LDS write
+      if (x < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global load
+    }
+    // step h = 1: publish stage s + 1
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if constexpr (!LAST) rfrag(F0, other, 0);
+    T.template mma<false>(F1);
+    if constexpr (!LAST) {
+#pragma unroll
+      for (int x = 0; x < kMfma; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (x < kDsReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+
+  gload(cur, 0);
+  swrite(slot0);
+  gload(cur, 1);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  rfrag(F0, slot0, 0);
+  for (int ti = 0; ti < count; ++ti) {
+    int cm0, cn0;
+    tile_mn(ti, cm0, cn0);
+    stage(IC<1>{}, IC<0>{}, 0, slot0, slot1);
+    stage(IC<0>{}, IC<0>{}, 1, slot1, slot0);
+    for (int s = 2; s < ns - 2; s += 2) {
+      stage(IC<0>{}, IC<0>{}, s, slot0, slot1);
+      stage(IC<0>{}, IC<0>{}, s + 1, slot1, slot0);
+    }
+    stage(IC<0>{}, IC<0>{}, ns - 2, slot0, slot1);
+    stage(IC<0>{}, IC<1>{}, ns - 1, slot1, slot0);
+    T.epilogue(cm0, cn0);
+    rfrag(F0, slot0, 0);               // the next tile's stage 0, published above
+    cur = nxt;
+    nxt = rows_of(ti + 2);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -527,6 +883,9 @@ using TwBig = PCfg<256, 256, 2, 4, 4, 0, 8, 0>;
 using TwBig2 = PCfg<256, 256, 2, 4, 2, 0, 8, 0>;
 using TwSmall = PCfg<128, 128, 2, 2, 4, 0, 8, 0>;
 using TwSmall2 = PCfg<128, 128, 2, 2, 2, 0, 8, 0>;
+// Fragment-pipelined: 256x256 tiles, 4 waves of 128x128 (one wave per SIMD).
+using TwWide = PCfg<256, 256, 2, 2, 5, 0, 8, 0>;
+using TwWide4 = PCfg<256, 256, 2, 2, 2, 0, 8, 0>;   // wide-stage kernel (its own LDS plan)
 // Block recipe: the partial sums need a second set of accumulators, so 256x128 tiles.
 // With one weight scale per 128 rows, 8 waves of 64x64; with a B scale per row (wgrad),
 // 8 waves of 128x32, so that a lane needs 16 B scales per 128-wide K block, not 32.
@@ -534,6 +893,52 @@ template <int BROWS> using Blk4 =
     PCfg<256, 128, BROWS == 1 ? 2 : 4, BROWS == 1 ? 4 : 2, 4, 0, 8, BROWS>;
 template <int BROWS> using Blk2 =
     PCfg<256, 128, BROWS == 1 ? 2 : 4, BROWS == 1 ? 4 : 2, 2, 0, 8, BROWS>;
+
+template <class C>
+hipError_t run_fpipe(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
+                     uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
+  const int tiles_m = (M + C::BM - 1) / C::BM;
+  const int tiles_n = (N + C::BN - 1) / C::BN;
+  const int tiles = tiles_m * tiles_n;
+  const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
+  int split_m = 0, split_n = 0;
+  static const bool split_on = env_flag("FP8LIN_GEMM_XCD_SPLIT", true);
+  if (grid == kMaxWorkgroups && split_on) {
+    int best = 1 << 30;
+    for (int pm = 1; pm <= 8; pm *= 2) {
+      const int pn = 8 / pm;
+      if (tiles_m % pm || tiles_n % pn) continue;
+      const int cost = (tiles_m / pm) * C::BM + (tiles_n / pn) * C::BN;
+      if (cost < best) { best = cost; split_m = pm; split_n = pn; }
+    }
+  }
+  hipLaunchKernelGGL(gemm_fp8_fpipe_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
+                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t run_wide(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
+                    uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
+  const int tiles_m = (M + C::BM - 1) / C::BM;
+  const int tiles_n = (N + C::BN - 1) / C::BN;
+  const int tiles = tiles_m * tiles_n;
+  const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
+  int split_m = 0, split_n = 0;
+  static const bool split_on = env_flag("FP8LIN_GEMM_XCD_SPLIT", true);
+  if (grid == kMaxWorkgroups && split_on) {
+    int best = 1 << 30;
+    for (int pm = 1; pm <= 8; pm *= 2) {
+      const int pn = 8 / pm;
+      if (tiles_m % pm || tiles_n % pn) continue;
+      const int cost = (tiles_m / pm) * C::BM + (tiles_n / pn) * C::BN;
+      if (cost < best) { best = cost; split_m = pm; split_n = pn; }
+    }
+  }
+  hipLaunchKernelGGL(gemm_fp8_wide_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
+                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  return hipGetLastError();
+}
 
 template <class C4, class C2>
 hipError_t run_tensorwise(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
@@ -550,8 +955,8 @@ hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const 
   // K is a multiple of 128 (checked on the host), so the step count is even
   // (the per-row B scale variant keeps two stages: four run out of registers)
   const int nk = K / kBKS;
-  if (BROWS != 1 && nk % 4 == 0)
-    return run_persist<Blk4<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
+  if constexpr (BROWS != 1)
+    if (nk % 4 == 0) return run_persist<Blk4<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
   return run_persist<Blk2<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
 }
 
@@ -569,6 +974,17 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, 
   int cfg = forced_cfg();
   if (cfg < 0) cfg = ((int64_t)M * N >= (int64_t)2048 * 2048) ? 0 : 1;
   if (cfg == 1) return run_tensorwise<TwSmall, TwSmall2>(A, B, sa, sb, D, m, n, k, mv, s);
+  if (cfg == 3) {
+    if (k % (2 * kStageK) == 0 && k >= 4 * kStageK)
+      return run_wide<TwWide4>(A, B, sa, sb, D, m, n, k, mv, s);
+    return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, D, m, n, k, mv, s);
+  }
+  if (cfg == 2) {
+    const int nk = (k + kBKS - 1) / kBKS;
+    if (nk % 2 == 0 && nk >= TwWide::STAGES && nk >= 6)
+      return run_fpipe<TwWide>(A, B, sa, sb, D, m, n, k, mv, s);
+    return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, D, m, n, k, mv, s);
+  }
   return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, D, m, n, k, mv, s);
 }
 
