@@ -39,7 +39,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the block-recipe and packed-varlen measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -375,7 +375,7 @@ def main():
     q_bytes_step = 4 * q_elems_step                # 2 B read + 1 B Q + 1 B Q^T per element
     q_ms_step = float(np.sum(q_ms)) / args.steps
     q_gbs = q_bytes_step / (q_ms_step * 1e-3) / 1e9
-    g_traffic = counter_traffic("gemm_fp8_persist_kernel")
+    g_traffic = counter_traffic("gemm_fp8_mx16_kernel")
     q_traffic = counter_traffic("quantize_tensorwise_kernel")
     line = {
         "metric": "fp8 linear fwd+bwd TFLOP/s at 8192x4096x14336; quantize+amax GB/s",
@@ -393,7 +393,7 @@ def main():
         "config": {"workload": "Llama-8B-shaped MLP block fwd+bwd (gate, up: 4096->14336; "
                                "down: 14336->4096), delayed tensorwise scaling",
                    "tokens": M, "K": K, "N": N, "linears": 3, "flops_per_step": flops_step},
-        "roofline": {"bound": "mfma", "kernel": "gemm_fp8_persist_kernel",
+        "roofline": {"bound": "mfma", "kernel": "gemm_fp8_mx16_kernel",
                      "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": g_traffic and g_traffic["bytes"],

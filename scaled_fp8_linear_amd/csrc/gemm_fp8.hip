@@ -16,26 +16,32 @@
 //     D[m, n] = bf16_rne( sum_kb sa[m, kb] * sb[n / b_rows, kb] * S_kb[m, n] ),
 // with b_rows = 128 for weight tiles and 1 for 1x128 tiles.
 //
-// Kernel design (both kernels share it):
-//  * macro tile BM x BN, K advances 64 bytes per step (one
-//    v_mfma_f32_32x32x64_f8f6f4 per 32x32 output tile and step);
-//  * operand tiles go from memory straight into LDS with buffer loads that
-//    carry the "lds" modifier (no VGPR staging, no ds_write), into a ring of
-//    STAGES separate LDS arrays; one wait + barrier per step publishes a stage;
-//  * each wavefront owns a (BM/WM) x (BN/WN) block of 32x32 output tiles. The
-//    B fragment is the instruction's first operand, so each lane holds 4
-//    consecutive n of one row m; the MFMA pairs A and B by lane and byte, so
-//    any ordering of k within a step is valid as long as both operands use it;
-//  * 64-byte LDS rows, 16-byte chunks XOR-swizzled by the row;
-//  * gemm_fp8_persist_kernel: one workgroup per CU walks its tiles as one
-//    stream of K steps (the next tile's loads overlap this tile's epilogue);
-//    each XCD gets a rectangle of output tiles (workgroups are dispatched
-//    round-robin over the 8 XCDs), so tiles that run together share A and B
-//    panels in that XCD's L2;
-//  * gemm_fp8_pipe_kernel: one tile per workgroup, for K step counts the
-//    persistent kernel's unrolled loop cannot divide;
-//  * epilogue: v_cvt_pk_bf16_f32 packs, v_permlane32_swap pairs lanes l and
-//    l + 32 so that every lane stores 16 contiguous bytes.
+// Kernels:
+//  * gemm_fp8_mx16_kernel (tensorwise, K a multiple of 256): 256x256 tiles, 4 waves of
+//    128x128 on v_mfma_f32_16x16x128_f8f6f4, 128-byte K stages in two LDS slots, one
+//    barrier per stage; described at the kernel;
+//  * gemm_fp8_persist_kernel (block recipe, and tensorwise for other K): macro tile
+//    BM x BN, K advances 64 bytes per step (one v_mfma_f32_32x32x64_f8f6f4 per 32x32
+//    output tile and step), a ring of STAGES LDS arrays, one wait + barrier per step;
+//  * gemm_fp8_pipe_kernel: one tile per workgroup, for K step counts the persistent
+//    kernel's unrolled loop cannot divide.
+// Shared by all three:
+//  * operand tiles go from memory straight into LDS with buffer loads that carry the
+//    "lds" modifier (no VGPR staging, no ds_write), issued through inline asm so the
+//    compiler does not add waits; the kernels wait (vmcnt) before the barrier that
+//    publishes a stage; rows past M or N, K tails and "no tile" read zeros through
+//    the buffer range check;
+//  * LDS rows XOR-swizzled by 16-byte chunk, so fragment reads are free of bank
+//    conflicts; the B fragment is the instruction's first operand, so each lane holds
+//    consecutive n of one row m; the MFMA pairs A and B by lane and byte, so any
+//    ordering of k within a step is valid as long as both operands use it;
+//  * persistent kernels: one workgroup per CU walks its tiles as one stream of K steps
+//    (the next tile's loads overlap this tile's epilogue); each XCD gets a rectangle of
+//    output tiles (workgroups are dispatched round-robin over the 8 XCDs), so tiles
+//    that run together share A and B panels in that XCD's L2;
+//  * epilogue: v_cvt_pk_bf16_f32 packs, a lane permute pairs results so that every
+//    lane stores 16 contiguous bytes through a buffer resource (pieces outside D are
+//    dropped by its range check); rows at or past M_valid are written as zeros.
 #include <stdlib.h>
 
 #include <type_traits>
@@ -50,6 +56,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit dwords
@@ -81,6 +88,15 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane((int)lds))
+               : "memory", "m0");
+}
+
+// As dma16, with a wave-uniform byte offset in an SGPR (added to the lane's offset; a
+// lane offset of 2^31 or more stays out of range, as the sum cannot wrap past 2^32).
+__device__ __forceinline__ void dma16_so(v4i rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(__builtin_amdgcn_readfirstlane((int)lds))
                : "memory", "m0");
 }
 
@@ -226,30 +242,6 @@ struct Tile {
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
     return v;
-  }
-
-  // operand fragments of one K step: the wave's TM A tiles and TN B tiles
-  struct Frags { v8i a[C::TM]; v8i b[C::TN]; };
-
-  __device__ void read_frags(Frags& F, const uint8_t* stage) const {
-    const uint8_t* pA = stage + (wm * C::WTM + fr) * kBKS;
-    const uint8_t* pB = stage + C::BM * kBKS + (wn * C::WTN + fr) * kBKS;
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) F.b[j] = frag(pB, 32 * j);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) F.a[i] = frag(pA, 32 * i);
-  }
-
-  // FIRST: the tile's first K step, which starts the sums from zero
-  template <bool FIRST>
-  __device__ void mma(const Frags& F) {
-    const v16f z = {};
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            F.b[j], F.a[i], FIRST ? z : acc[i][j], 0, 0, 0, 0, 0, 0);
   }
 
   // block recipe: load the scales of 128-wide K block kb of the tile at (m0, n0)
@@ -454,170 +446,54 @@ gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Persistent kernel with register-level fragment pipelining (tensorwise scaling).
-// Each wave keeps two fragment sets: while the MFMAs of K step j consume one, the
-// LDS reads of step j + 1 fill the other, interleaved one for one, so the matrix
-// cores and the LDS work at the same time.
-// LDS ring of STAGES slots, indexed at run time. At the top of step j a wave waits
-// for its own loads of step j + 1, and one barrier publishes that slot; the same
-// barrier frees the slot of step j - 1, whose fragments every wave has already fed
-// to the MFMAs of step j - 1, and that slot is refilled with step j + STAGES - 1.
-// So the barrier never waits on the LDS reads just issued for the next step.
-// A tile's bf16 stores (exactly 2 TM TN buffer stores per lane, in range or not) enter
-// the same in-order memory counter as the loads; for the first STAGES - 2 steps of the
-// next tile the waits allow them to stay in flight.
-template <class C>
-__global__ void __launch_bounds__(C::kThreads, 1)
-gemm_fp8_fpipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
-                      const float* __restrict__ sa, const float* __restrict__ sb,
-                      uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
-                      int tiles_n, int split_m, int split_n) {
-  static_assert(!C::BLOCK, "tensorwise only");
-  static_assert(C::STAGES >= 4, "two slots ahead of the refill");
-  constexpr int SB = C::kStageBytes;
-  constexpr int kStores = 2 * C::TM * C::TN;            // epilogue stores per lane
-  constexpr int kWaitN = C::kLoadsPerStage * (C::STAGES - 3);
-  static_assert(kWaitN + kStores <= 63, "vmcnt range");
-  constexpr int kDsReads = 2 * (C::TM + C::TN);
-  constexpr int kMfma = C::TM * C::TN;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::STAGES * SB];
-
-  Tile<C> T;
-  T.init(A, B, sa, sb, D, M, N, K, M_valid);
-
-  // tile assignment: as in gemm_fp8_persist_kernel (one rectangle of tiles per XCD)
-  const int nwg = gridDim.x;
-  int bm0 = 0, bn0 = 0, bmc = tiles_m, bnc = tiles_n, slot = blockIdx.x, nslots = nwg;
-  if (split_m > 0) {
-    const int xcd = blockIdx.x & 7;
-    const int rm = (tiles_m + split_m - 1) / split_m, rn = (tiles_n + split_n - 1) / split_n;
-    const int bx = xcd / split_n, by = xcd % split_n;
-    bm0 = bx * rm;
-    bn0 = by * rn;
-    bmc = max(0, min(tiles_m, bm0 + rm) - bm0);
-    bnc = max(0, min(tiles_n, bn0 + rn) - bn0);
-    slot = blockIdx.x >> 3;
-    nslots = nwg >> 3;
-  }
-  const int block_tiles = bmc * bnc;
-  const int count = slot < block_tiles ? (block_tiles - slot + nslots - 1) / nslots : 0;
-  auto tile_mn = [&](int ti, int& m0, int& n0) {
-    const int lid = slot + ti * nslots;
-    const int per_group = C::GROUP_M * bnc;
-    const int group = lid / per_group;
-    const int first_m = group * C::GROUP_M;
-    const int gsize = min(bmc - first_m, C::GROUP_M);
-    const int in_group = lid - group * per_group;
-    m0 = (bm0 + first_m + in_group % gsize) * C::BM;
-    n0 = (bn0 + in_group / gsize) * C::BN;
-  };
-  auto tile_base = [&](int ti) {
-    int m0 = 0, n0 = 0;
-    if (ti < count) tile_mn(ti, m0, n0);
-    return T.base(ti < count, m0, n0);
-  };
-
-  const int nk = T.nk;                 // even and >= STAGES (the host checks)
-  auto cur_tb = tile_base(0), next_tb = tile_base(1);
-  typename Tile<C>::Frags F0, F1;
-  int rd = 1, wr = C::STAGES - 1;      // slots of steps j + 1 and j - 1 (mod STAGES)
-
-  // One K step. FIRST: the tile's first step (sums start at zero). READ: fetch the next
-  // step's fragments (not at the tile's last step: they are fetched after the epilogue,
-  // so that they do not hold registers through it).
-  auto step = [&](auto FIRST_, auto READ_, typename Tile<C>::Frags& Fc,
-                  typename Tile<C>::Frags& Fn, int kk, bool loose) {
-    constexpr bool FIRST = decltype(FIRST_)::value != 0, READ = decltype(READ_)::value != 0;
-#ifndef FP8LIN_FPIPE_LOOSE
-#define FP8LIN_FPIPE_LOOSE 1
-#endif
-    if (FP8LIN_FPIPE_LOOSE && loose) wait_vm<kWaitN + kStores>();
-    else wait_vm<kWaitN>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const int kr = kk + C::STAGES - 1;                  // K step that refills slot wr
-    if (kr < nk) T.issue(smem + wr * SB, cur_tb, kr);
-    else T.issue(smem + wr * SB, next_tb, kr - nk);
-    if constexpr (READ) T.read_frags(Fn, smem + rd * SB);
-    T.template mma<FIRST>(Fc);
-    if constexpr (READ) {
-#pragma unroll
-      for (int x = 0; x < kMfma; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
-        if (x < kDsReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      }
-    }
-    rd = rd + 1 == C::STAGES ? 0 : rd + 1;
-    wr = wr + 1 == C::STAGES ? 0 : wr + 1;
-  };
-
-#pragma unroll
-  for (int i = 0; i < C::STAGES - 1; ++i) T.issue(smem + i * SB, cur_tb, i);
-  wait_vm<C::kLoadsPerStage * (C::STAGES - 2)>();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  T.read_frags(F0, smem);
-  for (int ti = 0; ti < count; ++ti) {
-    int cm0, cn0;
-    tile_mn(ti, cm0, cn0);
-    const bool after = ti > 0;   // the previous tile's stores may still be in flight
-    // steps 0, 1 | 2 .. nk - 3 | nk - 2, nk - 1 (nk is even and at least 6)
-    step(IC<1>{}, IC<1>{}, F0, F1, 0, after);
-    step(IC<0>{}, IC<1>{}, F1, F0, 1, after && 1 <= C::STAGES - 3);
-    for (int kk = 2; kk < nk - 2; kk += 2) {
-      step(IC<0>{}, IC<1>{}, F0, F1, kk, after && kk <= C::STAGES - 3);
-      step(IC<0>{}, IC<1>{}, F1, F0, kk + 1, after && kk + 1 <= C::STAGES - 3);
-    }
-    step(IC<0>{}, IC<1>{}, F0, F1, nk - 2, false);
-    step(IC<0>{}, IC<0>{}, F1, F0, nk - 1, false);
-    T.epilogue(cm0, cn0);
-    // the next tile's first fragments (K step nk, one slot behind rd, which has already
-    // moved on to step nk + 1); the barrier of step nk - 1 published that slot
-    T.read_frags(F0, smem + (rd == 0 ? C::STAGES - 1 : rd - 1) * SB);
-    cur_tb = next_tb;
-    next_tb = tile_base(ti + 2);
-  }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // no load may land after exit
-}
+constexpr int kStageK = 128;   // K bytes per LDS stage of gemm_fp8_mx16_kernel
 
 // ---------------------------------------------------------------------------
-// Wide-stage persistent kernel (tensorwise scaling), 256x256 tiles, 4 waves.
-// An LDS stage holds 128 K bytes of the tile's 256 A rows and 256 B rows (64 KB), so
-// every global load brings a whole 128-byte line per row: a 64-byte step would fetch
-// each line in two halves, one step apart, which halves the L2 -> CU throughput.
-// Two LDS slots. Stage s + 1 waits in VGPRs (one 16-byte buffer load per lane and
-// 32 rows) while stage s is multiplied, is written to the free slot at the start of
-// stage s, and the loads of stage s + 2 go out right after; they have two MFMA steps
-// to land. One barrier per stage, in its middle: it publishes stage s + 1 and, as
-// every wave has finished its LDS reads of stage s - 1 before it, frees that slot. Within a stage, the two 64-byte MFMA steps are fragment-pipelined as in
-// gemm_fp8_fpipe_kernel. LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled
-// by (row / 2) % 8, which keeps both the row-wise writes and the fragment reads free
-// of bank conflicts. The loads go through the compiler, which places their waits.
-constexpr int kStageK = 128;
-
+// 16x16x128 kernel (tensorwise scaling): 256x256 tiles, 4 waves of 128x128, each wave
+// an 8x8 grid of v_mfma_f32_16x16x128_f8f6f4 tiles (the 16x16 form keeps the matrix
+// cores busier than 32x32x64 when LDS reads run alongside, and moves half as many
+// accumulator bytes per FLOP). An LDS stage holds 128 K bytes of the tile's 256 A and
+// 256 B rows (64 KB), in two slots, loaded straight to LDS: a 64-byte K step would
+// fetch each 128-byte line in two halves, one step apart, which halves the L2 -> CU
+// throughput. One MFMA covers a whole stage's K, so per stage a wave runs
+// 64 MFMAs (rows i = 0..7 of 16x16 tiles, all 8 columns j each):
+//   first half  (rows 0..3): A fragments of rows 4..7 are read in between;
+//   mid-stage:  the wave waits for its loads of stage s + 1; a barrier publishes them
+//               and frees this stage's slot (all its reads are done by then);
+//   second half (rows 4..7): the loads of stage s + 2 go into this slot, and stage
+//               s + 1's B fragments and rows 0..3 of its A fragments are read.
+// B fragments of a stage stay in registers for all 64 MFMAs (two sets alternate).
+// Fragment of a 16-row tile: lane l holds 32 bytes of row l % 16 at K offset
+// 32 (l / 16); the instruction pairs A and B by lane and byte, so this K order is as
+// good as any. The B tile goes in as the first operand, so a lane's 4 results are 4
+// consecutive n of row m = l % 16.
 template <class C>
 __global__ void __launch_bounds__(C::kThreads, 1)
-gemm_fp8_wide_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                      const float* __restrict__ sa, const float* __restrict__ sb,
                      uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
                      int tiles_n, int split_m, int split_n) {
   static_assert(!C::BLOCK, "tensorwise only");
   constexpr int SB = (C::BM + C::BN) * kStageK;
-  constexpr int kPassRows = C::kThreads / 8;                 // rows per load pass
-  constexpr int kPassA = C::BM / kPassRows, kPassB = C::BN / kPassRows;
-  constexpr int kLoads = kPassA + kPassB;
-  constexpr int kDsReads = 2 * (C::TM + C::TN);
-  constexpr int kMfma = C::TM * C::TN;
-  static_assert(C::BM % kPassRows == 0 && C::BN % kPassRows == 0, "load passes");
-  // two slots as two arrays, so that the compiler sees that the reads of one and the
-  // writes of the other never alias (and can interleave them)
+  constexpr int kRowsPerInst = 1024 / kStageK;               // 8 rows of 128 bytes
+  constexpr int kInstA = C::BM / (kRowsPerInst * C::kWaves);  // per wave and stage
+  constexpr int kInstB = C::BN / (kRowsPerInst * C::kWaves);
+  constexpr int kDma = kInstA + kInstB;
+  constexpr int RT = C::WTM / 16, CT = C::WTN / 16;           // 16x16 tiles per wave
+  constexpr int RH = RT / 2;                                  // rows per half stage
+  constexpr int kStores = RT * CT / 2;                        // epilogue stores per lane
+  static_assert(RT % 2 == 0 && kDma <= 63 && kStores <= 63, "plan");
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[SB];
 
-  Tile<C> T;
-  T.init(A, B, sa, sb, D, M, N, K, M_valid);
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, M * K, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, N * K, kRsrcWord3);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const v4i rsA = make_rsrc(A, (uint32_t)(M * K));
+  const v4i rsB = make_rsrc(B, (uint32_t)(N * K));
+  const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc(D, 0, M * N * 2, kRsrcWord3);
+  const float scl = __builtin_bit_cast(
+      float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sa[0] * sb[0])));
 
   // tile assignment: as in gemm_fp8_persist_kernel (one rectangle of tiles per XCD)
   const int nwg = gridDim.x;
@@ -646,131 +522,191 @@ gemm_fp8_wide_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     n0 = (bn0 + in_group / gsize) * C::BN;
   };
 
-  // load plan: lane t takes 16-byte chunk t % 8 of rows t / 8 + 32 i
-  const int t = threadIdx.x;
-  const int lrow = t >> 3, lch = t & 7;
-  const uint32_t st_off = (uint32_t)(lrow * kStageK + 16 * (lch ^ ((lrow >> 1) & 7)));
-  struct Rows { uint32_t a, b; };     // byte offsets of this lane's first rows, K block 0
+  // load plan: instruction i of wave w fills rows
+  // 8 (W i + w) .. + 8; lane l writes 16 bytes at 16 l: row l / 8, physical chunk l % 8,
+  // which holds logical chunk (l % 8) ^ ((row / 2) % 8)
+  const int lrow = kRowsPerInst * wave + (lane >> 3);
+  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
+  const uint32_t inst_rows = (uint32_t)(kRowsPerInst * C::kWaves) * (uint32_t)K;
+  struct Rows { uint32_t a, b; };
   auto rows_of = [&](int ti) -> Rows {
     if (ti >= count) return {kOutOfRange, kOutOfRange};
     int m0, n0;
     tile_mn(ti, m0, n0);
-    return {(uint32_t)(m0 + lrow) * (uint32_t)K + 16u * lch,
-            (uint32_t)(n0 + lrow) * (uint32_t)K + 16u * lch};
+    return {(uint32_t)(m0 + lrow) * (uint32_t)K + 16u * lchunk,
+            (uint32_t)(n0 + lrow) * (uint32_t)K + 16u * lchunk};
   };
-  const uint32_t pass_step = (uint32_t)kPassRows * (uint32_t)K;
-  using u4 = decltype(__builtin_amdgcn_raw_buffer_load_b128(rA, 0, 0, 0));
-  u4 buf[kLoads];
-  auto gload = [&](Rows r, int kb) {
-    const bool ok = r.a != kOutOfRange;
+  // load d (0 .. kDma) of stage kb of the tile whose rows are r, into slot_mem; the
+  // row group and K block part of the offset is wave-uniform and goes in an SGPR
+  auto dma = [&](int d, uint8_t* slot_mem, Rows r, int kb) {
     const uint32_t k0 = (uint32_t)kb * kStageK;
-#pragma unroll
-    for (int i = 0; i < kPassA; ++i)
-      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, ok ? r.a + i * pass_step + k0 : kOutOfRange,
-                                                     0, 0);
-#pragma unroll
-    for (int i = 0; i < kPassB; ++i)
-      buf[kPassA + i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rB, ok ? r.b + i * pass_step + k0 : kOutOfRange, 0, 0);
+    const uint32_t lds = lds_addr(slot_mem) + 1024u * wave;
+    if (d < kInstA)
+      dma16_so(rsA, r.a, d * inst_rows + k0, lds + 1024u * C::kWaves * d);
+    else
+      dma16_so(rsB, r.b, (d - kInstA) * inst_rows + k0,
+               lds + C::BM * kStageK + 1024u * C::kWaves * (d - kInstA));
   };
-  auto swrite = [&](uint8_t* slot_mem) {
-    uint8_t* base = slot_mem + st_off;
-#pragma unroll
-    for (int i = 0; i < kPassA; ++i)
-      *reinterpret_cast<u4*>(base + i * kPassRows * kStageK) = buf[i];
-#pragma unroll
-    for (int i = 0; i < kPassB; ++i)
-      *reinterpret_cast<u4*>(base + C::BM * kStageK + i * kPassRows * kStageK) = buf[kPassA + i];
+  // fragments: lane (r16 = l % 16, g = l / 16) reads logical chunks 2 g, 2 g + 1 of its row;
+  // rows 16 apart share the swizzle
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int sw = (r16 >> 1) & 7;
+  const uint32_t fo0 = r16 * kStageK + 16 * ((2 * g4) ^ sw);
+  const uint32_t fo1 = r16 * kStageK + 16 * ((2 * g4 + 1) ^ sw);
+  auto rd = [&](const uint8_t* p) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(p + fo0);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p + fo1);
+    v8i v;
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    return v;
   };
-  // fragment reads: lane (fr, fg) takes logical chunks 4 h + 2 fg and 4 h + 2 fg + 1 of
-  // its row for MFMA step h of the stage; rows 32 apart share the swizzle
-  const int sw = (T.fr >> 1) & 7;
-  const uint32_t fo00 = T.fr * kStageK + 16 * ((2 * T.fg) ^ sw);
-  const uint32_t fo01 = T.fr * kStageK + 16 * ((2 * T.fg + 1) ^ sw);
-  const uint32_t fo10 = T.fr * kStageK + 16 * ((4 + 2 * T.fg) ^ sw);
-  const uint32_t fo11 = T.fr * kStageK + 16 * ((4 + 2 * T.fg + 1) ^ sw);
-  auto rfrag = [&](typename Tile<C>::Frags& F, const uint8_t* slot_mem, int h) {
-    const uint8_t* pa = slot_mem + (T.wm * C::WTM) * kStageK;
-    const uint8_t* pb = slot_mem + (C::BM + T.wn * C::WTN) * kStageK;
-    const uint32_t o0 = h ? fo10 : fo00, o1 = h ? fo11 : fo01;
-    auto rd = [&](const uint8_t* p) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(p + o0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(p + o1);
-      v8i v;
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      return v;
-    };
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) F.b[j] = rd(pb + 32 * j * kStageK);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) F.a[i] = rd(pa + 32 * i * kStageK);
+  auto rdA = [&](const uint8_t* sm, int i) { return rd(sm + (wm * C::WTM + 16 * i) * kStageK); };
+  auto rdB = [&](const uint8_t* sm, int j) {
+    return rd(sm + (C::BM + wn * C::WTN + 16 * j) * kStageK);
   };
+
+  v4f acc[RT][CT];
+  // B fragments of this stage and the next (two sets alternate); A rows 0 .. RH-1 of
+  // the next stage are read after this stage's are used, so one set serves
+  v8i Bf0[CT], Bf1[CT], Alo[RH], Ahi[RH];
 
   const int ns = K / kStageK;          // stages per tile: even and >= 4 (the host checks)
   Rows cur = rows_of(0), nxt = rows_of(1);
-  typename Tile<C>::Frags F0, F1;
 
-  // One stage (two MFMA steps) on slot `mine`, the other slot being `other`. Tiles have
-  // an even number of stages, so stage s of every tile uses slot s % 2. FIRST: the
-  // tile's first stage. LAST: its last stage, whose second step fetches no fragments
-  // (the next tile's come after the epilogue).
-  auto stage = [&](auto FIRST_, auto LAST_, int s, uint8_t* mine, uint8_t* other) {
+  // One stage. Bc and Alo: this stage's B fragments and A rows 0 .. RH-1 (read before);
+  // Bn and Alo: the next stage's, read in the second half.
+  // FIRST: the tile's first stage (sums start at zero; after a previous tile, that
+  // tile's kStores stores are the newest memory operations, issued after the loads this
+  // stage waits for: loads and stores retire in order, so they may stay in flight).
+  // LAST: the tile's last stage, which reads no fragments of the next stage (they are
+  // read after the epilogue, so that they hold no registers through it).
+  auto stage = [&](auto FIRST_, auto LAST_, int s, uint8_t* mine, uint8_t* other, v8i* Bc,
+                   v8i* Bn, bool after) {
     constexpr bool FIRST = decltype(FIRST_)::value != 0, LAST = decltype(LAST_)::value != 0;
-    // step h = 0. `other` is already free: its last reads (the previous stage's second
-    // half) were issued before the previous stage's barrier, which each wave passed only
-    // after all of its LDS operations had completed.
-    rfrag(F1, mine, 1);
-    swrite(other);                     // stage s + 1 (loaded during stage s - 1)
-    const int g = s + 2;               // stage to load now: of this tile or of the next
-    gload(g < ns ? cur : nxt, g < ns ? g : g - ns);
-    T.template mma<FIRST>(F0);
+    const v4f z = {};
+    // first half: rows 0 .. RH-1; A rows RH .. RT-1 are read in between
 #pragma unroll
-    for (int x = 0; x < kMfma; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-      if (x < kDsReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
-      if (x < kLoads) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // LDS write
-      if (x < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global load
+    for (int i = 0; i < RH; ++i) Ahi[i] = rdA(mine, RH + i);
+#pragma unroll
+    for (int i = 0; i < RH; ++i)
+#pragma unroll
+      for (int j = 0; j < CT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Alo[i],
+                                                                     FIRST ? z : acc[i][j], 0, 0,
+                                                                     0, 0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < RH * CT; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (x % (CT / 2) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // step h = 1: publish stage s + 1
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // stage s + 1 landed (own loads), own LDS reads done; then for every wave
+    if (FIRST && after) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStores) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if constexpr (!LAST) rfrag(F0, other, 0);
-    T.template mma<false>(F1);
-    if constexpr (!LAST) {
+    // second half: rows RH .. RT-1, with the loads of stage s + 2 (into `mine`) and the
+    // reads of stage s + 1's fragments (from `other`) in between, in a pinned order
+    const int gs = s + 2;
+    const Rows r = gs < ns ? cur : nxt;
+    const int kb = gs < ns ? gs : gs - ns;
+    constexpr int kSecond = RH * CT;                 // MFMAs in the second half
+    constexpr int kReads = CT + RH;                  // fragments to read
 #pragma unroll
-      for (int x = 0; x < kMfma; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (x < kDsReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int x = 0; x < kSecond; ++x) {
+      const int i = RH + x / CT, j = x % CT;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Ahi[i - RH],
+                                                                   FIRST ? z : acc[i][j], 0, 0, 0,
+                                                                   0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (x * kDma / kSecond != (x + 1) * kDma / kSecond) dma(x * kDma / kSecond, mine, r, kb);
+      if (!LAST && x * kReads / kSecond != (x + 1) * kReads / kSecond) {
+        const int f = x * kReads / kSecond;
+        if (f < CT) Bn[f] = rdB(other, f);
+        else Alo[f - CT] = rdA(other, f - CT);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  gload(cur, 0);
-  swrite(slot0);
-  gload(cur, 1);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // epilogue: scale, round to bf16, 16-byte stores. Tiles j and j + 1 of a row go
+  // together: after v_permlane16_swap on their packed results, lane group g (= l / 16)
+  // holds 8 consecutive n, namely columns 8 (g / 2) .. + 8 of tile j + g % 2. Tiles
+  // wholly inside the valid rows and D take a path without per-piece checks.
+  static_assert(CT % 2 == 0, "tile pairs");
+  auto epilogue = [&](int m0, int n0) {
+    const bool full = m0 + C::BM <= M_valid && n0 + C::BN <= N;   // M_valid <= M
+    const int mrow = m0 + wm * C::WTM + r16;
+    const int ncol = n0 + wn * C::WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
+    const uint32_t base = ((uint32_t)mrow * (uint32_t)N + (uint32_t)ncol) * 2u;
+    auto piece = [&](int i, int jp) {
+      const int j = 2 * jp;
+      const uint32_t p0j = pack_bf16x2(acc[i][j][0] * scl, acc[i][j][1] * scl);
+      const uint32_t p1j = pack_bf16x2(acc[i][j][2] * scl, acc[i][j][3] * scl);
+      const uint32_t p0k = pack_bf16x2(acc[i][j + 1][0] * scl, acc[i][j + 1][1] * scl);
+      const uint32_t p1k = pack_bf16x2(acc[i][j + 1][2] * scl, acc[i][j + 1][3] * scl);
+      const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
+      const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
+      return v4i{(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
+    };
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int jp = 0; jp < CT / 2; ++jp)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              piece(i, jp), rsD, base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int jp = 0; jp < CT / 2; ++jp) {
+          const int m = mrow + 16 * i, n = ncol + 32 * jp;
+          v4i o = piece(i, jp);
+          if (m >= M_valid) o = v4i{0, 0, 0, 0};
+          const uint32_t off = (m < M && n < N)
+                                   ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp
+                                   : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
+        }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) dma(d, slot0, cur, 0);
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) dma(d, slot1, ns > 1 ? cur : nxt, ns > 1 ? 1 : 0);
+  wait_vm<kDma>();                     // stage 0 landed
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  rfrag(F0, slot0, 0);
+  // stage 0 of a tile: its B fragments and A rows 0 .. RH-1 (slot 0, published)
+  auto first_frags = [&]() {
+#pragma unroll
+    for (int j = 0; j < CT; ++j) Bf0[j] = rdB(slot0, j);
+#pragma unroll
+    for (int i = 0; i < RH; ++i) Alo[i] = rdA(slot0, i);
+  };
+  first_frags();
   for (int ti = 0; ti < count; ++ti) {
     int cm0, cn0;
     tile_mn(ti, cm0, cn0);
-    stage(IC<1>{}, IC<0>{}, 0, slot0, slot1);
-    stage(IC<0>{}, IC<0>{}, 1, slot1, slot0);
+    const bool after = ti > 0;
+    // stages 0, 1 | 2 .. ns - 3 | ns - 2, ns - 1 (ns is even and at least 4)
+    stage(IC<1>{}, IC<0>{}, 0, slot0, slot1, Bf0, Bf1, after);
+    stage(IC<0>{}, IC<0>{}, 1, slot1, slot0, Bf1, Bf0, false);
     for (int s = 2; s < ns - 2; s += 2) {
-      stage(IC<0>{}, IC<0>{}, s, slot0, slot1);
-      stage(IC<0>{}, IC<0>{}, s + 1, slot1, slot0);
+      stage(IC<0>{}, IC<0>{}, s, slot0, slot1, Bf0, Bf1, false);
+      stage(IC<0>{}, IC<0>{}, s + 1, slot1, slot0, Bf1, Bf0, false);
     }
-    stage(IC<0>{}, IC<0>{}, ns - 2, slot0, slot1);
-    stage(IC<0>{}, IC<1>{}, ns - 1, slot1, slot0);
-    T.epilogue(cm0, cn0);
-    rfrag(F0, slot0, 0);               // the next tile's stage 0, published above
+    stage(IC<0>{}, IC<0>{}, ns - 2, slot0, slot1, Bf0, Bf1, false);
+    stage(IC<0>{}, IC<1>{}, ns - 1, slot1, slot0, Bf1, Bf0, false);
+    epilogue(cm0, cn0);
+    first_frags();                     // the next tile's stage 0, published at stage ns - 1
     cur = nxt;
     nxt = rows_of(ti + 2);
   }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // no load may land after exit
 }
 
 // ---------------------------------------------------------------------------
@@ -883,9 +819,8 @@ using TwBig = PCfg<256, 256, 2, 4, 4, 0, 8, 0>;
 using TwBig2 = PCfg<256, 256, 2, 4, 2, 0, 8, 0>;
 using TwSmall = PCfg<128, 128, 2, 2, 4, 0, 8, 0>;
 using TwSmall2 = PCfg<128, 128, 2, 2, 2, 0, 8, 0>;
-// Fragment-pipelined: 256x256 tiles, 4 waves of 128x128 (one wave per SIMD).
-using TwWide = PCfg<256, 256, 2, 2, 5, 0, 8, 0>;
-using TwWide4 = PCfg<256, 256, 2, 2, 2, 0, 8, 0>;   // wide-stage kernel (its own LDS plan)
+// 16x16x128 kernel: 256x256 tiles, 4 waves of 128x128 (its own LDS plan).
+using TwMx16 = PCfg<256, 256, 2, 2, 2, 0, 8, 0>;
 // Block recipe: the partial sums need a second set of accumulators, so 256x128 tiles.
 // With one weight scale per 128 rows, 8 waves of 64x64; with a B scale per row (wgrad),
 // 8 waves of 128x32, so that a lane needs 16 B scales per 128-wide K block, not 32.
@@ -895,30 +830,7 @@ template <int BROWS> using Blk2 =
     PCfg<256, 128, BROWS == 1 ? 2 : 4, BROWS == 1 ? 4 : 2, 2, 0, 8, BROWS>;
 
 template <class C>
-hipError_t run_fpipe(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
-                     uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
-  const int tiles_m = (M + C::BM - 1) / C::BM;
-  const int tiles_n = (N + C::BN - 1) / C::BN;
-  const int tiles = tiles_m * tiles_n;
-  const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
-  int split_m = 0, split_n = 0;
-  static const bool split_on = env_flag("FP8LIN_GEMM_XCD_SPLIT", true);
-  if (grid == kMaxWorkgroups && split_on) {
-    int best = 1 << 30;
-    for (int pm = 1; pm <= 8; pm *= 2) {
-      const int pn = 8 / pm;
-      if (tiles_m % pm || tiles_n % pn) continue;
-      const int cost = (tiles_m / pm) * C::BM + (tiles_n / pn) * C::BN;
-      if (cost < best) { best = cost; split_m = pm; split_n = pn; }
-    }
-  }
-  hipLaunchKernelGGL(gemm_fp8_fpipe_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
-                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
-  return hipGetLastError();
-}
-
-template <class C>
-hipError_t run_wide(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
+hipError_t run_mx16(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
                     uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + C::BN - 1) / C::BN;
@@ -935,7 +847,7 @@ hipError_t run_wide(const uint8_t* A, const uint8_t* B, const float* sa, const f
       if (cost < best) { best = cost; split_m = pm; split_n = pn; }
     }
   }
-  hipLaunchKernelGGL(gemm_fp8_wide_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
+  hipLaunchKernelGGL(gemm_fp8_mx16_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
                      B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   return hipGetLastError();
 }
@@ -971,20 +883,16 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, 
     if (b_rows_per_scale == 1) return run_block<1>(A, B, sa, sb, D, m, n, k, mv, s);
     return run_block<128>(A, B, sa, sb, D, m, n, k, mv, s);
   }
+  // tensorwise: the 16x16x128 kernel where its stage plan fits (K a multiple of 256, at
+  // least 512) and the output spans at least 64 of its tiles; else the 32x32x64
+  // persistent kernel with 256x256 tiles, or 128x128 tiles for small outputs.
+  // FP8LIN_GEMM_CFG (0: 256x256, 1: 128x128, 2: 16x16x128) forces a choice for sweeps.
+  const bool mx16_ok = k % (2 * kStageK) == 0 && k >= 4 * kStageK;
+  const bool big = (int64_t)M * N >= (int64_t)2048 * 2048;
   int cfg = forced_cfg();
-  if (cfg < 0) cfg = ((int64_t)M * N >= (int64_t)2048 * 2048) ? 0 : 1;
+  if (cfg < 0) cfg = big ? (mx16_ok ? 2 : 0) : 1;
+  if (cfg == 2 && mx16_ok) return run_mx16<TwMx16>(A, B, sa, sb, D, m, n, k, mv, s);
   if (cfg == 1) return run_tensorwise<TwSmall, TwSmall2>(A, B, sa, sb, D, m, n, k, mv, s);
-  if (cfg == 3) {
-    if (k % (2 * kStageK) == 0 && k >= 4 * kStageK)
-      return run_wide<TwWide4>(A, B, sa, sb, D, m, n, k, mv, s);
-    return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, D, m, n, k, mv, s);
-  }
-  if (cfg == 2) {
-    const int nk = (k + kBKS - 1) / kBKS;
-    if (nk % 2 == 0 && nk >= TwWide::STAGES && nk >= 6)
-      return run_fpipe<TwWide>(A, B, sa, sb, D, m, n, k, mv, s);
-    return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, D, m, n, k, mv, s);
-  }
   return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, D, m, n, k, mv, s);
 }
 

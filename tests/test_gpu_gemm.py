@@ -139,3 +139,50 @@ def test_full_size_headline_sampled(lib):
         D = gemm.scaled_gemm(a, bq, sx, sw)[0, 0]
         bound = gemm.error_bound(a, bq, sx, sb=sw)[0, 0]
         assert abs(yh[m, n] - D) <= bound, (m, n, yh[m, n], D, bound)
+
+
+# Shapes the 16x16x128 kernel takes (output of at least 2048 x 2048, K a multiple of 256
+# and at least 512), with ragged M and N (partial 256-row / 256-column tiles) and with
+# padded rows (M_valid < M).
+@pytest.mark.parametrize("M,N,K,mv", [(2064, 2320, 512, 2064), (2320, 2064, 768, 2301),
+                                      (4096, 1040, 1024, 4000)])
+def test_wide_kernel_ragged(lib, M, N, K, mv):
+    qa, sa = _codes((M, K), 31 + M, "student_t", nu=3)
+    qb, sb = _codes((N, K), 32 + N, "normal", std=0.02)
+    note(f"fp8_linear_fwd M={M} N={N} K={K} M_valid={mv}")
+    y = lib.fp8_linear_fwd(_dev(qa), _dev(qb), dev_f32(sa), dev_f32(sb), M_valid=mv)
+    torch.cuda.synchronize()
+    yh = host_bf16_f64(y)
+    assert np.all(yh[mv:] == 0)
+    D, b = _exact_and_bound(qa[:mv], qb, sa, sb)
+    worst = assert_within(yh[:mv], D, b, f"fwd {M}x{N}x{K}")
+    assert worst < 0.25
+
+
+@pytest.mark.parametrize("M,N,K,what", [(8192, 4096, 14336, "dgrad"), (14336, 4096, 8192, "wgrad")])
+def test_full_size_backward_shapes_sampled(lib, M, N, K, what):
+    """The MLP block's dgrad (contraction over 14336) and wgrad (contraction over the 8192
+    tokens) launch shapes: operands quantized on the GPU (bit-exact with the oracle, see
+    test_gpu_quantize), 1024 sampled outputs computed one by one by the oracle from the
+    sampled rows."""
+    from oracle.quantize import quantize_values
+    a = workloads.bf16_tensor("normal", (M, K), 3, 41 + K, 0, std=1e-3)
+    b = workloads.bf16_tensor("student_t", (N, K), 3, 42 + K, 0, nu=3)
+    sa, sai = scale_from_amax(o_amax(a))
+    sb, sbi = scale_from_amax(o_amax(b))
+    note(f"full size {what}: quantize operands on the GPU")
+    ad = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    bd = torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+    qa, _, _, _, _ = lib.fp8_quantize_amax(ad, scale_inv=dev_f32(sai), want_q_t=False)
+    qb, _, _, _, _ = lib.fp8_quantize_amax(bd, scale_inv=dev_f32(sbi), want_q_t=False)
+    note(f"full size {what}: fp8 GEMM {M}x{N}x{K}")
+    y = lib.fp8_linear_fwd(qa, qb, dev_f32(sa), dev_f32(sb))
+    torch.cuda.synchronize()
+    yh = host_bf16_f64(y)
+    rng = np.random.default_rng(K)
+    for m, n in zip(rng.integers(0, M, 1024), rng.integers(0, N, 1024)):
+        ra = quantize_values(a[m:m + 1], sai)
+        rb = quantize_values(b[n:n + 1], sbi)
+        D = gemm.scaled_gemm(ra, rb, sa, sb)[0, 0]
+        bound = gemm.error_bound(ra, rb, sa, sb)[0, 0]
+        assert abs(yh[m, n] - D) <= bound, (what, m, n, yh[m, n], D, bound)
