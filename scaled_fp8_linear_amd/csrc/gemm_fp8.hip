@@ -100,6 +100,14 @@ __device__ __forceinline__ void dma16_so(v4i rsrc, uint32_t voff, uint32_t soff,
                : "memory", "m0");
 }
 
+// One 4-byte-per-lane buffer load written straight to LDS at lds + 4 * lane.
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane((int)lds))
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   // this wave's loads older than the newest N have landed
@@ -710,6 +718,338 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Block-recipe 16x16x128 kernel: 256x128 tiles, 8 waves (two per SIMD) of 64x64, each a
+// 4x4 grid of 16x16 tiles. A 16x16x128 MFMA covers exactly one 128-wide K block, so
+// each one, started from zero, is that block's partial sum P, and the lane folds it in
+//     acc += P * (sa[m, kb] * sb[n / b_rows, kb])
+// with the accumulators in VGPRs (64 per wave, which is what lets P and the fragments
+// stay in VGPRs as well: each MFMA then has its own result registers and the folds of
+// one MFMA overlap the next). Stages of 128 K bytes as in gemm_fp8_mx16_kernel, but in
+// three LDS slots: the barrier in the middle of stage s publishes stage s + 1 and frees
+// slot s % 3, which takes the loads of stage s + 3, so two stages are in flight while
+// one is multiplied (with one, the load latency, not the matrix cores, sets the pace).
+// The slot index is computed at run time (the compiler sees no LDS writes: the loads
+// are asm). A slot also holds the stage's scales, loaded with the operands by 4-byte
+// LDS loads into one region indexed by p = 64 w + l (wave w, lane l):
+//   p in [0, BM):       sa of tile row wm WTM + 16 (p % RT) + (p % WTM) / RT, for
+//                       p = wm WTM + (row % 16) RT + i: a lane's RT row scales are
+//                       contiguous;
+//   p in [BM, BM + BN): with one scale per B row, sb of tile column
+//                       wn WTN + 16 j + 4 g + r at p - BM = wn WTN + g 4 CT + 4 j + r
+//                       (a lane's 4 CT column scales are contiguous); with one scale
+//                       per 128 B rows, the single value at p = BM.
+// Every wave issues the same loads per stage (lanes with nothing to load read out of
+// range), so the memory counts stay uniform.
+template <class C>
+__global__ void __launch_bounds__(C::kThreads, 1)
+gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                      const float* __restrict__ sa, const float* __restrict__ sb,
+                      uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
+                      int tiles_n, int split_m, int split_n) {
+  static_assert(C::BLOCK, "block recipe");
+  constexpr int BROWS = C::BROWS;
+  constexpr int RT = C::WTM / 16, CT = C::WTN / 16;
+  constexpr int RH = RT / 2;
+  constexpr int kTileBytes = (C::BM + C::BN) * kStageK;
+  constexpr int kScaleLanes = 64 * C::kWaves;
+  constexpr int kSaOff = kTileBytes, kSbOff = kTileBytes + 4 * C::BM;
+  constexpr int SB = kTileBytes + 4 * kScaleLanes;
+  constexpr int kRowsPerInst = 1024 / kStageK;
+  constexpr int kInstA = C::BM / (kRowsPerInst * C::kWaves);
+  constexpr int kInstB = C::BN / (kRowsPerInst * C::kWaves);
+  constexpr int kDma = kInstA + kInstB + 1;                   // + one scale piece
+  constexpr int kStores = RT * CT / 2;
+  static_assert(RT % 2 == 0 && CT % 2 == 0 && 2 * kDma + kStores <= 63, "plan");
+  static_assert(C::BM + C::BN <= kScaleLanes, "one scale load per wave and stage");
+  static_assert(C::BM % (kRowsPerInst * C::kWaves) == 0 &&
+                C::BN % (kRowsPerInst * C::kWaves) == 0, "load instructions");
+  static_assert(BROWS == 1 || C::BN % BROWS == 0, "one weight scale row per tile");
+  constexpr int kSlots = 3;             // two stages in flight while one is multiplied
+  static_assert(kSlots * SB <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * SB];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int kblocks = K / kStageK;
+  const v4i rsA = make_rsrc(A, (uint32_t)(M * K));
+  const v4i rsB = make_rsrc(B, (uint32_t)(N * K));
+  const v4i rsSa = make_rsrc(sa, (uint32_t)(M * kblocks * 4));
+  const v4i rsSb = make_rsrc(sb, (uint32_t)(((N + BROWS - 1) / BROWS) * kblocks * 4));
+  const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc(D, 0, M * N * 2, kRsrcWord3);
+
+  // tile assignment: as in gemm_fp8_persist_kernel (one rectangle of tiles per XCD)
+  const int nwg = gridDim.x;
+  int bm0 = 0, bn0 = 0, bmc = tiles_m, bnc = tiles_n, slot = blockIdx.x, nslots = nwg;
+  if (split_m > 0) {
+    const int xcd = blockIdx.x & 7;
+    const int rm = (tiles_m + split_m - 1) / split_m, rn = (tiles_n + split_n - 1) / split_n;
+    const int bx = xcd / split_n, by = xcd % split_n;
+    bm0 = bx * rm;
+    bn0 = by * rn;
+    bmc = max(0, min(tiles_m, bm0 + rm) - bm0);
+    bnc = max(0, min(tiles_n, bn0 + rn) - bn0);
+    slot = blockIdx.x >> 3;
+    nslots = nwg >> 3;
+  }
+  const int block_tiles = bmc * bnc;
+  const int count = slot < block_tiles ? (block_tiles - slot + nslots - 1) / nslots : 0;
+  auto tile_mn = [&](int ti, int& m0, int& n0) {
+    const int lid = slot + ti * nslots;
+    const int per_group = C::GROUP_M * bnc;
+    const int group = lid / per_group;
+    const int first_m = group * C::GROUP_M;
+    const int gsize = min(bmc - first_m, C::GROUP_M);
+    const int in_group = lid - group * per_group;
+    m0 = (bm0 + first_m + in_group % gsize) * C::BM;
+    n0 = (bn0 + in_group / gsize) * C::BN;
+  };
+
+  // operand load plan: as gemm_fp8_mx16_kernel
+  const int lrow = kRowsPerInst * wave + (lane >> 3);
+  const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
+  const uint32_t inst_rows = (uint32_t)(kRowsPerInst * C::kWaves) * (uint32_t)K;
+  // scale load plan (see above)
+  const int p = 64 * wave + lane;
+  struct Rows { uint32_t a, b, sc; };   // this lane's byte offsets for K block 0
+  auto rows_of = [&](int ti) -> Rows {
+    if (ti >= count) return {kOutOfRange, kOutOfRange, kOutOfRange};
+    int m0, n0;
+    tile_mn(ti, m0, n0);
+    uint32_t osc = kOutOfRange;
+    if (p < C::BM) {
+      const int q = p % C::WTM;
+      const int row = (p / C::WTM) * C::WTM + 16 * (q % RT) + q / RT;
+      osc = (uint32_t)(m0 + row) * (uint32_t)kblocks * 4u;
+    } else if constexpr (BROWS == 1) {
+      if (p < C::BM + C::BN) {
+        const int q = p - C::BM, qw = q % C::WTN;
+        const int col = (q / C::WTN) * C::WTN + 16 * ((qw % (4 * CT)) / 4) + 4 * (qw / (4 * CT)) +
+                        (qw % 4);
+        osc = (uint32_t)(n0 + col) * (uint32_t)kblocks * 4u;
+      }
+    } else {
+      if (p == C::BM) osc = (uint32_t)(n0 / BROWS) * (uint32_t)kblocks * 4u;
+    }
+    return {(uint32_t)(m0 + lrow) * (uint32_t)K + 16u * lchunk,
+            (uint32_t)(n0 + lrow) * (uint32_t)K + 16u * lchunk, osc};
+  };
+  // the scale piece of wave w reads from sa (waves holding p < BM) or sb
+  const bool sc_from_a = 64 * wave < C::BM;
+  static_assert(C::BM % 64 == 0, "a wave's scale lanes come from one grid");
+  auto dma = [&](int d, uint8_t* slot_mem, Rows r, int kb) {
+    const uint32_t k0 = (uint32_t)kb * kStageK;
+    const uint32_t lds = lds_addr(slot_mem);
+    if (d < kInstA)
+      dma16_so(rsA, r.a, d * inst_rows + k0, lds + 1024u * wave + 1024u * C::kWaves * d);
+    else if (d < kInstA + kInstB)
+      dma16_so(rsB, r.b, (d - kInstA) * inst_rows + k0,
+               lds + C::BM * kStageK + 1024u * wave + 1024u * C::kWaves * (d - kInstA));
+    else
+      dma4(sc_from_a ? rsSa : rsSb, r.sc == kOutOfRange ? kOutOfRange : r.sc + 4u * kb,
+           lds + kSaOff + 256u * wave);
+  };
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int sw = (r16 >> 1) & 7;
+  const uint32_t fo0 = r16 * kStageK + 16 * ((2 * g4) ^ sw);
+  const uint32_t fo1 = r16 * kStageK + 16 * ((2 * g4 + 1) ^ sw);
+  auto rd = [&](const uint8_t* q) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(q + fo0);
+    const uint4 hi = *reinterpret_cast<const uint4*>(q + fo1);
+    v8i v;
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    return v;
+  };
+  auto rdA = [&](const uint8_t* sm, int i) { return rd(sm + (wm * C::WTM + 16 * i) * kStageK); };
+  auto rdB = [&](const uint8_t* sm, int j) {
+    return rd(sm + (C::BM + wn * C::WTN + 16 * j) * kStageK);
+  };
+  // this stage's scales: fa[i] = sa of the lane's row in tile row i (times sb when B has one
+  // scale per tile), fb the lane's column scales when B has one per row
+  float fa[RT];
+  float fb[BROWS == 1 ? CT * 4 : 1];
+  auto rd_scales = [&](const uint8_t* sm) {
+    static_assert(RT % 4 == 0, "row scales by 16 bytes");
+    const float4* qa = reinterpret_cast<const float4*>(sm + kSaOff + 4 * (wm * C::WTM + r16 * RT));
+#pragma unroll
+    for (int v = 0; v < RT / 4; ++v) {
+      const float4 a4 = qa[v];
+      fa[4 * v + 0] = a4.x; fa[4 * v + 1] = a4.y; fa[4 * v + 2] = a4.z; fa[4 * v + 3] = a4.w;
+    }
+    if constexpr (BROWS == 1) {
+      const float4* qb =
+          reinterpret_cast<const float4*>(sm + kSbOff + 4 * (wn * C::WTN + g4 * 4 * CT));
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        const float4 b4 = qb[j];
+        fb[4 * j + 0] = b4.x; fb[4 * j + 1] = b4.y; fb[4 * j + 2] = b4.z; fb[4 * j + 3] = b4.w;
+      }
+    } else {
+      fb[0] = *reinterpret_cast<const float*>(sm + kSbOff);
+    }
+  };
+
+  v4f acc[RT][CT];
+  v8i Bf0[CT], Bf1[CT], Alo[RH], Ahi[RH];
+  const int ns = K / kStageK;          // stages per tile: even and >= 4 (the host checks)
+  Rows cur = rows_of(0), nxt = rows_of(1);
+
+  // MFMA x of the stage (x = i CT + j) gives the block's partial sum P; fold() adds it in
+  // with its scale. Software-pipelined: MFMA x is issued before the fold of MFMA x - 1.
+  auto mfma_x = [&](int x, const v8i* Bc) {
+    const int i = x / CT, j = x % CT;
+    const v4f z = {};
+    const v8i& a = i < RH ? Alo[i] : Ahi[i - RH];
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], a, z, 0, 0, 0, 0, 0, 0);
+  };
+  auto fold = [&](auto FIRST_, int x, const v4f& P) {
+    constexpr bool FIRST = decltype(FIRST_)::value != 0;
+    const int i = x / CT, j = x % CT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float f;
+      if constexpr (BROWS == 1) f = fa[i] * fb[4 * j + r];
+      else f = fa[i];                   // sb is folded into fa once per stage
+      acc[i][j][r] = FIRST ? P[r] * f : fmaf(P[r], f, acc[i][j][r]);
+    }
+  };
+
+  auto stage = [&](auto FIRST_, auto LAST_, int s, uint8_t* mine, uint8_t* other, v8i* Bc,
+                   v8i* Bn, bool after) {
+    constexpr bool LAST = decltype(LAST_)::value != 0;
+    constexpr bool FIRST = decltype(FIRST_)::value != 0;
+    constexpr int kHalf = RH * CT;       // MFMAs per half stage
+    v4f P[2];
+    // first half: rows 0 .. RH-1; this stage's scales, then A rows RH .. RT-1, are read
+    rd_scales(mine);
+#pragma unroll
+    for (int i = 0; i < RH; ++i) Ahi[i] = rdA(mine, RH + i);
+    if constexpr (BROWS != 1) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) fa[i] *= fb[0];
+    }
+#pragma unroll
+    for (int x = 0; x < kHalf; ++x) {
+      P[x & 1] = mfma_x(x, Bc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (x > 0) fold(FIRST_, x - 1, P[(x - 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // own loads of stage s + 1 landed (those of stage s + 2, and after a previous tile
+    // its stores, which were issued later, may stay in flight: they retire in order)
+    if (FIRST && after)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kDma + kStores) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kDma) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // second half: rows RH .. RT-1, with the loads of stage s + 3 (into `mine`) and the
+    // reads of stage s + 1's first fragments in between
+    const int gs = s + kSlots;
+    const Rows r = gs < ns ? cur : nxt;
+    const int kb = gs < ns ? gs : gs - ns;
+    constexpr int kReads = CT + RH;
+#pragma unroll
+    for (int y = 0; y < kHalf; ++y) {
+      const int x = kHalf + y;
+      P[x & 1] = mfma_x(x, Bc);
+      __builtin_amdgcn_sched_barrier(0);
+      fold(FIRST_, x - 1, P[(x - 1) & 1]);
+#pragma unroll
+      for (int d = y * kDma / kHalf; d < (y + 1) * kDma / kHalf; ++d) dma(d, mine, r, kb);
+#pragma unroll
+      for (int f = y * kReads / kHalf; f < (y + 1) * kReads / kHalf; ++f) {
+        if constexpr (!LAST) {
+          if (f < CT) Bn[f] = rdB(other, f);
+          else Alo[f - CT] = rdA(other, f - CT);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fold(FIRST_, 2 * kHalf - 1, P[(2 * kHalf - 1) & 1]);
+  };
+
+  auto epilogue = [&](int m0, int n0) {
+    const bool full = m0 + C::BM <= M_valid && n0 + C::BN <= N;
+    const int mrow = m0 + wm * C::WTM + r16;
+    const int ncol = n0 + wn * C::WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
+    const uint32_t base = ((uint32_t)mrow * (uint32_t)N + (uint32_t)ncol) * 2u;
+    auto piece = [&](int i, int jp) {
+      const int j = 2 * jp;
+      const uint32_t p0j = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+      const uint32_t p1j = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      const uint32_t p0k = pack_bf16x2(acc[i][j + 1][0], acc[i][j + 1][1]);
+      const uint32_t p1k = pack_bf16x2(acc[i][j + 1][2], acc[i][j + 1][3]);
+      const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
+      const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
+      return v4i{(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
+    };
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int jp = 0; jp < CT / 2; ++jp)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              piece(i, jp), rsD, base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int jp = 0; jp < CT / 2; ++jp) {
+          const int m = mrow + 16 * i, n = ncol + 32 * jp;
+          v4i o = piece(i, jp);
+          if (m >= M_valid) o = v4i{0, 0, 0, 0};
+          const uint32_t off = (m < M && n < N)
+                                   ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp
+                                   : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
+        }
+    }
+  };
+
+  // global stage counter g: stage g lives in slot g % 3
+  auto slot_of = [&](int g) { return smem + (g % kSlots) * SB; };
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) dma(d, smem, cur, 0);
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) dma(d, smem + SB, cur, 1);
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) dma(d, smem + 2 * SB, cur, 2);
+  wait_vm<2 * kDma>();                 // stage 0 landed
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  int g = 0;                           // global index of the tile's first stage
+  auto first_frags = [&]() {
+    uint8_t* sm = slot_of(g);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) Bf0[j] = rdB(sm, j);
+#pragma unroll
+    for (int i = 0; i < RH; ++i) Alo[i] = rdA(sm, i);
+  };
+  first_frags();
+  for (int ti = 0; ti < count; ++ti) {
+    int cm0, cn0;
+    tile_mn(ti, cm0, cn0);
+    const bool after = ti > 0;
+    // stages 0, 1 | 2 .. ns - 3 | ns - 2, ns - 1 (ns is even and at least 4)
+    stage(IC<1>{}, IC<0>{}, 0, slot_of(g), slot_of(g + 1), Bf0, Bf1, after);
+    stage(IC<0>{}, IC<0>{}, 1, slot_of(g + 1), slot_of(g + 2), Bf1, Bf0, false);
+    for (int s = 2; s < ns - 2; s += 2) {
+      stage(IC<0>{}, IC<0>{}, s, slot_of(g + s), slot_of(g + s + 1), Bf0, Bf1, false);
+      stage(IC<0>{}, IC<0>{}, s + 1, slot_of(g + s + 1), slot_of(g + s + 2), Bf1, Bf0, false);
+    }
+    stage(IC<0>{}, IC<0>{}, ns - 2, slot_of(g + ns - 2), slot_of(g + ns - 1), Bf0, Bf1, false);
+    stage(IC<0>{}, IC<1>{}, ns - 1, slot_of(g + ns - 1), slot_of(g + ns), Bf1, Bf0, false);
+    epilogue(cm0, cn0);
+    g += ns;
+    first_frags();                     // the next tile's stage 0, published at stage ns - 1
+    cur = nxt;
+    nxt = rows_of(ti + 2);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // no load may land after exit
+}
+
+// ---------------------------------------------------------------------------
 // One tile per workgroup; K steps past the end are zero loads, so the loop body
 // (unrolled by STAGES) needs no branches. Tensorwise scaling only.
 template <class C>
@@ -861,11 +1201,40 @@ hipError_t run_tensorwise(const uint8_t* A, const uint8_t* B, const float* sa, c
   return run_pipe<C2>(A, B, sa, sb, D, M, N, K, M_valid, s);
 }
 
+template <class C>
+hipError_t run_mx16b(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
+                     uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
+  const int tiles_m = (M + C::BM - 1) / C::BM;
+  const int tiles_n = (N + C::BN - 1) / C::BN;
+  const int tiles = tiles_m * tiles_n;
+  const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
+  int split_m = 0, split_n = 0;
+  static const bool split_on = env_flag("FP8LIN_GEMM_XCD_SPLIT", true);
+  if (grid == kMaxWorkgroups && split_on) {
+    int best = 1 << 30;
+    for (int pm = 1; pm <= 8; pm *= 2) {
+      const int pn = 8 / pm;
+      if (tiles_m % pm || tiles_n % pn) continue;
+      const int cost = (tiles_m / pm) * C::BM + (tiles_n / pn) * C::BN;
+      if (cost < best) { best = cost; split_m = pm; split_n = pn; }
+    }
+  }
+  hipLaunchKernelGGL(gemm_fp8_mx16b_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
+                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  return hipGetLastError();
+}
+
+// block recipe on the 16x16x128 kernel: 256x128 tiles, 8 waves of 64x64
+template <int BROWS> using BlkMx16 = PCfg<256, 128, 4, 2, 2, 0, 8, BROWS>;
+
 template <int BROWS>
 hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
                      uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
   // K is a multiple of 128 (checked on the host), so the step count is even
   // (the per-row B scale variant keeps two stages: four run out of registers)
+  static const int forced = forced_cfg();
+  if (K % (2 * kStageK) == 0 && K >= 4 * kStageK && forced != 0)
+    return run_mx16b<BlkMx16<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
   const int nk = K / kBKS;
   if constexpr (BROWS != 1)
     if (nk % 4 == 0) return run_persist<Blk4<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);

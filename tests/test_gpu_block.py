@@ -86,6 +86,14 @@ def test_block_linear_step(lib, M, K, N, rv):
     assert_within(host_bf16_f64(dw), r["dw"], wb, "block wgrad")
 
 
+@pytest.mark.parametrize("M,K,N,rv", [(2176, 768, 1152, 2176), (1408, 1024, 2304, 1350),
+                                      (1536, 768, 1280, 1500)])
+def test_block_linear_step_wide_kernel(lib, M, K, N, rv):
+    """Shapes the 16x16x128 block kernel takes (contraction a multiple of 256, >= 512):
+    rows ragged against its 256-row tiles, padded token rows, all three GEMMs."""
+    test_block_linear_step(lib, M, K, N, rv)
+
+
 def test_block_full_size_sampled(lib):
     """The block recipe at its benchmark size (M=16384, K=N=8192, outliers x100 at 1%):
     tile grids bit-exact on sampled tiles, GEMM outputs on sampled elements."""
