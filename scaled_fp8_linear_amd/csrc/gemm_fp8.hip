@@ -91,8 +91,9 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
                : "memory", "m0");
 }
 
-// As dma16, with a wave-uniform byte offset in an SGPR (added to the lane's offset; a
-// lane offset of 2^31 or more stays out of range, as the sum cannot wrap past 2^32).
+// As dma16, with a wave-uniform byte offset in an SGPR added to the lane's. Callers put
+// the whole row offset in the lane's operand (the one the buffer range check is sure to
+// test) and only an offset that stays inside a row in the SGPR.
 __device__ __forceinline__ void dma16_so(v4i rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
@@ -536,23 +537,26 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   const int lrow = kRowsPerInst * wave + (lane >> 3);
   const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
   const uint32_t inst_rows = (uint32_t)(kRowsPerInst * C::kWaves) * (uint32_t)K;
-  struct Rows { uint32_t a, b; };
+  // the lane's part of its row offsets (the same for A and B)
+  const uint32_t lane_off = (uint32_t)lrow * (uint32_t)K + 16u * lchunk;
+  struct Rows { uint32_t a, b; };      // wave-uniform: the tile's first row times K
   auto rows_of = [&](int ti) -> Rows {
     if (ti >= count) return {kOutOfRange, kOutOfRange};
     int m0, n0;
     tile_mn(ti, m0, n0);
-    return {(uint32_t)(m0 + lrow) * (uint32_t)K + 16u * lchunk,
-            (uint32_t)(n0 + lrow) * (uint32_t)K + 16u * lchunk};
+    return {(uint32_t)m0 * (uint32_t)K, (uint32_t)n0 * (uint32_t)K};
   };
-  // load d (0 .. kDma) of stage kb of the tile whose rows are r, into slot_mem; the
-  // row group and K block part of the offset is wave-uniform and goes in an SGPR
+  // load d (0 .. kDma) of stage kb of the tile whose rows are r, into slot_mem. The lane's
+  // whole row offset goes in the VGPR operand, which the buffer range check tests, so
+  // rows past M or N read zeros; only the K block's offset (which stays inside a row)
+  // goes in the SGPR operand.
   auto dma = [&](int d, uint8_t* slot_mem, Rows r, int kb) {
     const uint32_t k0 = (uint32_t)kb * kStageK;
     const uint32_t lds = lds_addr(slot_mem) + 1024u * wave;
     if (d < kInstA)
-      dma16_so(rsA, r.a, d * inst_rows + k0, lds + 1024u * C::kWaves * d);
+      dma16_so(rsA, lane_off + (r.a + d * inst_rows), k0, lds + 1024u * C::kWaves * d);
     else
-      dma16_so(rsB, r.b, (d - kInstA) * inst_rows + k0,
+      dma16_so(rsB, lane_off + (r.b + (d - kInstA) * inst_rows), k0,
                lds + C::BM * kStageK + 1024u * C::kWaves * (d - kInstA));
   };
   // fragments: lane (r16 = l % 16, g = l / 16) reads logical chunks 2 g, 2 g + 1 of its row;
@@ -577,13 +581,16 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   v4f acc[RT][CT];
   // B fragments of this stage and the next (two sets alternate); A rows 0 .. RH-1 of
   // the next stage are read after this stage's are used, so one set serves
+  // B fragments of this stage and the next (two sets alternate); A rows 0 .. RH-1 and
+  // RH .. RT-1 of this stage. Only B and A row 0 are read a stage ahead: rows 1 .. RT-1
+  // are read during the stage's first half, which keeps the register peak down.
   v8i Bf0[CT], Bf1[CT], Alo[RH], Ahi[RH];
 
   const int ns = K / kStageK;          // stages per tile: even and >= 4 (the host checks)
   Rows cur = rows_of(0), nxt = rows_of(1);
 
-  // One stage. Bc and Alo: this stage's B fragments and A rows 0 .. RH-1 (read before);
-  // Bn and Alo: the next stage's, read in the second half.
+  // One stage. Bc and Alo[0]: this stage's B fragments and A row 0 (read before); Bn and
+  // Alo[0]: the next stage's, read in the second half.
   // FIRST: the tile's first stage (sums start at zero; after a previous tile, that
   // tile's kStores stores are the newest memory operations, issued after the loads this
   // stage waits for: loads and stores retire in order, so they may stay in flight).
@@ -593,7 +600,10 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
                    v8i* Bn, bool after) {
     constexpr bool FIRST = decltype(FIRST_)::value != 0, LAST = decltype(LAST_)::value != 0;
     const v4f z = {};
-    // first half: rows 0 .. RH-1; A rows RH .. RT-1 are read in between
+    // first half: rows 0 .. RH-1; A rows 1 .. RT-1 are read in between (row i is first
+    // needed by MFMA i CT, and is read among the first ones)
+#pragma unroll
+    for (int i = 1; i < RH; ++i) Alo[i] = rdA(mine, i);
 #pragma unroll
     for (int i = 0; i < RH; ++i) Ahi[i] = rdA(mine, RH + i);
 #pragma unroll
@@ -606,7 +616,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 #pragma unroll
     for (int x = 0; x < RH * CT; ++x) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (x % (CT / 2) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (x % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // stage s + 1 landed (own loads), own LDS reads done; then for every wave
@@ -620,7 +630,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     const Rows r = gs < ns ? cur : nxt;
     const int kb = gs < ns ? gs : gs - ns;
     constexpr int kSecond = RH * CT;                 // MFMAs in the second half
-    constexpr int kReads = CT + RH;                  // fragments to read
+    constexpr int kReads = CT + 1;                   // fragments to read
 #pragma unroll
     for (int x = 0; x < kSecond; ++x) {
       const int i = RH + x / CT, j = x % CT;
@@ -640,44 +650,38 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 
   // epilogue: scale, round to bf16, 16-byte stores. Tiles j and j + 1 of a row go
   // together: after v_permlane16_swap on their packed results, lane group g (= l / 16)
-  // holds 8 consecutive n, namely columns 8 (g / 2) .. + 8 of tile j + g % 2. Tiles
-  // wholly inside the valid rows and D take a path without per-piece checks.
+  // holds 8 consecutive n, namely columns 8 (g / 2) .. + 8 of tile j + g % 2. One code
+  // path for every tile (a second one would have the compiler compute all 256 scaled
+  // values up front for both): rows at or past M_valid are replaced by zeros, pieces
+  // outside D get an offset past its end, which the range check drops.
   static_assert(CT % 2 == 0, "tile pairs");
   auto epilogue = [&](int m0, int n0) {
-    const bool full = m0 + C::BM <= M_valid && n0 + C::BN <= N;   // M_valid <= M
     const int mrow = m0 + wm * C::WTM + r16;
     const int ncol = n0 + wn * C::WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
     const uint32_t base = ((uint32_t)mrow * (uint32_t)N + (uint32_t)ncol) * 2u;
-    auto piece = [&](int i, int jp) {
-      const int j = 2 * jp;
-      const uint32_t p0j = pack_bf16x2(acc[i][j][0] * scl, acc[i][j][1] * scl);
-      const uint32_t p1j = pack_bf16x2(acc[i][j][2] * scl, acc[i][j][3] * scl);
-      const uint32_t p0k = pack_bf16x2(acc[i][j + 1][0] * scl, acc[i][j + 1][1] * scl);
-      const uint32_t p1k = pack_bf16x2(acc[i][j + 1][2] * scl, acc[i][j + 1][3] * scl);
-      const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
-      const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
-      return v4i{(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
-    };
-    if (full) {
 #pragma unroll
-      for (int i = 0; i < RT; ++i)
+    for (int i = 0; i < RT; ++i) {
+      const int m = mrow + 16 * i;
+      const bool live = m < M_valid;   // rows past it are written as zeros, whatever
+                                       // their sums hold (a select, not a product)
+      const float si = scl;
 #pragma unroll
-        for (int jp = 0; jp < CT / 2; ++jp)
-          __builtin_amdgcn_raw_buffer_store_b128(
-              piece(i, jp), rsD, base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int jp = 0; jp < CT / 2; ++jp) {
-          const int m = mrow + 16 * i, n = ncol + 32 * jp;
-          v4i o = piece(i, jp);
-          if (m >= M_valid) o = v4i{0, 0, 0, 0};
-          const uint32_t off = (m < M && n < N)
-                                   ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp
-                                   : kOutOfRange;
-          __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
-        }
+      for (int jp = 0; jp < CT / 2; ++jp) {
+        const int j = 2 * jp;
+        const uint32_t p0j = pack_bf16x2(acc[i][j][0] * si, acc[i][j][1] * si);
+        const uint32_t p1j = pack_bf16x2(acc[i][j][2] * si, acc[i][j][3] * si);
+        const uint32_t p0k = pack_bf16x2(acc[i][j + 1][0] * si, acc[i][j + 1][1] * si);
+        const uint32_t p1k = pack_bf16x2(acc[i][j + 1][2] * si, acc[i][j + 1][3] * si);
+        const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
+        const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
+        v4i o = {(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
+        if (!live) o = v4i{0, 0, 0, 0};
+        const bool in = m < M && ncol + 32 * jp < N;
+        const uint32_t off =
+            in ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -692,8 +696,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   auto first_frags = [&]() {
 #pragma unroll
     for (int j = 0; j < CT; ++j) Bf0[j] = rdB(slot0, j);
-#pragma unroll
-    for (int i = 0; i < RH; ++i) Alo[i] = rdA(slot0, i);
+    Alo[0] = rdA(slot0, 0);
   };
   first_frags();
   for (int ti = 0; ti < count; ++ti) {
@@ -811,42 +814,54 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   const uint32_t inst_rows = (uint32_t)(kRowsPerInst * C::kWaves) * (uint32_t)K;
   // scale load plan (see above)
   const int p = 64 * wave + lane;
-  struct Rows { uint32_t a, b, sc; };   // this lane's byte offsets for K block 0
+  // the lane's parts of its offsets: operand rows (the same for A and B) and its scale
+  // (tile row or column times the scale grid's row bytes; kOutOfRange: nothing to load)
+  const uint32_t lane_off = (uint32_t)lrow * (uint32_t)K + 16u * lchunk;
+  // the scale piece of wave w reads from sa (waves holding p < BM) or sb
+  const bool sc_from_a = 64 * wave < C::BM;
+  static_assert(C::BM % 64 == 0, "a wave's scale lanes come from one grid");
+  uint32_t sc_lane = kOutOfRange;
+  if (p < C::BM) {
+    const int q = p % C::WTM;
+    const int row = (p / C::WTM) * C::WTM + 16 * (q % RT) + q / RT;
+    sc_lane = (uint32_t)row * (uint32_t)kblocks * 4u;
+  } else if constexpr (BROWS == 1) {
+    if (p < C::BM + C::BN) {
+      const int q = p - C::BM, qw = q % C::WTN;
+      const int col = (q / C::WTN) * C::WTN + 16 * ((qw % (4 * CT)) / 4) + 4 * (qw / (4 * CT)) +
+                      (qw % 4);
+      sc_lane = (uint32_t)col * (uint32_t)kblocks * 4u;
+    }
+  } else {
+    if (p == C::BM) sc_lane = 0;
+  }
+  struct Rows { uint32_t a, b, sc; };   // wave-uniform parts for the tile (K block 0)
   auto rows_of = [&](int ti) -> Rows {
     if (ti >= count) return {kOutOfRange, kOutOfRange, kOutOfRange};
     int m0, n0;
     tile_mn(ti, m0, n0);
-    uint32_t osc = kOutOfRange;
-    if (p < C::BM) {
-      const int q = p % C::WTM;
-      const int row = (p / C::WTM) * C::WTM + 16 * (q % RT) + q / RT;
-      osc = (uint32_t)(m0 + row) * (uint32_t)kblocks * 4u;
-    } else if constexpr (BROWS == 1) {
-      if (p < C::BM + C::BN) {
-        const int q = p - C::BM, qw = q % C::WTN;
-        const int col = (q / C::WTN) * C::WTN + 16 * ((qw % (4 * CT)) / 4) + 4 * (qw / (4 * CT)) +
-                        (qw % 4);
-        osc = (uint32_t)(n0 + col) * (uint32_t)kblocks * 4u;
-      }
-    } else {
-      if (p == C::BM) osc = (uint32_t)(n0 / BROWS) * (uint32_t)kblocks * 4u;
-    }
-    return {(uint32_t)(m0 + lrow) * (uint32_t)K + 16u * lchunk,
-            (uint32_t)(n0 + lrow) * (uint32_t)K + 16u * lchunk, osc};
+    uint32_t sc;
+    if (sc_from_a) sc = (uint32_t)m0 * (uint32_t)kblocks * 4u;
+    else if constexpr (BROWS == 1) sc = (uint32_t)n0 * (uint32_t)kblocks * 4u;
+    else sc = (uint32_t)(n0 / BROWS) * (uint32_t)kblocks * 4u;
+    return {(uint32_t)m0 * (uint32_t)K, (uint32_t)n0 * (uint32_t)K, sc};
   };
-  // the scale piece of wave w reads from sa (waves holding p < BM) or sb
-  const bool sc_from_a = 64 * wave < C::BM;
-  static_assert(C::BM % 64 == 0, "a wave's scale lanes come from one grid");
+  // load d of stage kb: whole row offsets in the VGPR operand, which the buffer range
+  // check tests (rows past M or N read zeros); only the K block's offset, which stays
+  // inside a row, in the SGPR operand
   auto dma = [&](int d, uint8_t* slot_mem, Rows r, int kb) {
     const uint32_t k0 = (uint32_t)kb * kStageK;
     const uint32_t lds = lds_addr(slot_mem);
     if (d < kInstA)
-      dma16_so(rsA, r.a, d * inst_rows + k0, lds + 1024u * wave + 1024u * C::kWaves * d);
+      dma16_so(rsA, lane_off + (r.a + d * inst_rows), k0,
+               lds + 1024u * wave + 1024u * C::kWaves * d);
     else if (d < kInstA + kInstB)
-      dma16_so(rsB, r.b, (d - kInstA) * inst_rows + k0,
+      dma16_so(rsB, lane_off + (r.b + (d - kInstA) * inst_rows), k0,
                lds + C::BM * kStageK + 1024u * wave + 1024u * C::kWaves * (d - kInstA));
     else
-      dma4(sc_from_a ? rsSa : rsSb, r.sc == kOutOfRange ? kOutOfRange : r.sc + 4u * kb,
+      dma4(sc_from_a ? rsSa : rsSb,
+           (sc_lane == kOutOfRange || r.sc == kOutOfRange) ? kOutOfRange
+                                                           : sc_lane + r.sc + 4u * kb,
            lds + kSaOff + 256u * wave);
   };
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -969,41 +984,33 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
     fold(FIRST_, 2 * kHalf - 1, P[(2 * kHalf - 1) & 1]);
   };
 
+  // epilogue: as gemm_fp8_mx16_kernel's (the block scales are already applied)
   auto epilogue = [&](int m0, int n0) {
-    const bool full = m0 + C::BM <= M_valid && n0 + C::BN <= N;
     const int mrow = m0 + wm * C::WTM + r16;
     const int ncol = n0 + wn * C::WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
     const uint32_t base = ((uint32_t)mrow * (uint32_t)N + (uint32_t)ncol) * 2u;
-    auto piece = [&](int i, int jp) {
-      const int j = 2 * jp;
-      const uint32_t p0j = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-      const uint32_t p1j = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-      const uint32_t p0k = pack_bf16x2(acc[i][j + 1][0], acc[i][j + 1][1]);
-      const uint32_t p1k = pack_bf16x2(acc[i][j + 1][2], acc[i][j + 1][3]);
-      const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
-      const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
-      return v4i{(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
-    };
-    if (full) {
 #pragma unroll
-      for (int i = 0; i < RT; ++i)
+    for (int i = 0; i < RT; ++i) {
+      const int m = mrow + 16 * i;
+      const bool live = m < M_valid;   // rows past it are written as zeros, whatever
+                                       // their sums hold (a select, not a product)
 #pragma unroll
-        for (int jp = 0; jp < CT / 2; ++jp)
-          __builtin_amdgcn_raw_buffer_store_b128(
-              piece(i, jp), rsD, base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int jp = 0; jp < CT / 2; ++jp) {
-          const int m = mrow + 16 * i, n = ncol + 32 * jp;
-          v4i o = piece(i, jp);
-          if (m >= M_valid) o = v4i{0, 0, 0, 0};
-          const uint32_t off = (m < M && n < N)
-                                   ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp
-                                   : kOutOfRange;
-          __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
-        }
+      for (int jp = 0; jp < CT / 2; ++jp) {
+        const int j = 2 * jp;
+        const uint32_t p0j = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        const uint32_t p1j = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        const uint32_t p0k = pack_bf16x2(acc[i][j + 1][0], acc[i][j + 1][1]);
+        const uint32_t p1k = pack_bf16x2(acc[i][j + 1][2], acc[i][j + 1][3]);
+        const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
+        const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
+        v4i o = {(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
+        if (!live) o = v4i{0, 0, 0, 0};
+        const bool in = m < M && ncol + 32 * jp < N;
+        const uint32_t off =
+            in ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
