@@ -17,10 +17,11 @@
 // with b_rows = 128 for weight tiles and 1 for 1x128 tiles.
 //
 // Kernels:
-//  * gemm_fp8_mx16_kernel (tensorwise, K a multiple of 256): 256x256 tiles, 4 waves of
+//  * gemm_fp8_mx16_kernel (tensorwise, K of at least 512): 256x256 tiles, 4 waves of
 //    128x128 on v_mfma_f32_16x16x128_f8f6f4, 128-byte K stages in two LDS slots, one
 //    barrier per stage; described at the kernel;
-//  * gemm_fp8_persist_kernel (block recipe, and tensorwise for other K): macro tile
+//  * gemm_fp8_mx16b_kernel (block recipe, K of at least 512): 256x128 tiles, 8 waves;
+//  * gemm_fp8_persist_kernel (small outputs and K): macro tile
 //    BM x BN, K advances 64 bytes per step (one v_mfma_f32_32x32x64_f8f6f4 per 32x32
 //    output tile and step), a ring of STAGES LDS arrays, one wait + barrier per step;
 //  * gemm_fp8_pipe_kernel: one tile per workgroup, for K step counts the persistent
@@ -476,7 +477,7 @@ constexpr int kStageK = 128;   // K bytes per LDS stage of gemm_fp8_mx16_kernel
 // 32 (l / 16); the instruction pairs A and B by lane and byte, so this K order is as
 // good as any. The B tile goes in as the first operand, so a lane's 4 results are 4
 // consecutive n of row m = l % 16.
-template <class C>
+template <class C, bool TAIL>
 __global__ void __launch_bounds__(C::kThreads, 1)
 gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                      const float* __restrict__ sa, const float* __restrict__ sb,
@@ -553,11 +554,15 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   auto dma = [&](int d, uint8_t* slot_mem, Rows r, int kb) {
     const uint32_t k0 = (uint32_t)kb * kStageK;
     const uint32_t lds = lds_addr(slot_mem) + 1024u * wave;
+    uint32_t off = d < kInstA ? lane_off + (r.a + d * inst_rows)
+                              : lane_off + (r.b + (d - kInstA) * inst_rows);
+    // TAIL (K not a multiple of 256): the K tail, or a padding stage, reads zeros, chunk
+    // by chunk (K is a multiple of 16)
+    if constexpr (TAIL) off = k0 + 16u * lchunk < (uint32_t)K ? off : kOutOfRange;
     if (d < kInstA)
-      dma16_so(rsA, lane_off + (r.a + d * inst_rows), k0, lds + 1024u * C::kWaves * d);
+      dma16_so(rsA, off, k0, lds + 1024u * C::kWaves * d);
     else
-      dma16_so(rsB, lane_off + (r.b + (d - kInstA) * inst_rows), k0,
-               lds + C::BM * kStageK + 1024u * C::kWaves * (d - kInstA));
+      dma16_so(rsB, off, k0, lds + C::BM * kStageK + 1024u * C::kWaves * (d - kInstA));
   };
   // fragments: lane (r16 = l % 16, g = l / 16) reads logical chunks 2 g, 2 g + 1 of its row;
   // rows 16 apart share the swizzle
@@ -586,7 +591,9 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // are read during the stage's first half, which keeps the register peak down.
   v8i Bf0[CT], Bf1[CT], Alo[RH], Ahi[RH];
 
-  const int ns = K / kStageK;          // stages per tile: even and >= 4 (the host checks)
+  // stages per tile: K / 128 rounded up to an even count of at least 4; stages past K
+  // (the tail of a K that is not a multiple of 256) load zeros
+  const int ns = max(4, (((K + kStageK - 1) / kStageK) + 1) & ~1);
   Rows cur = rows_of(0), nxt = rows_of(1);
 
   // One stage. Bc and Alo[0]: this stage's B fragments and A row 0 (read before); Bn and
@@ -851,17 +858,18 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   // inside a row, in the SGPR operand
   auto dma = [&](int d, uint8_t* slot_mem, Rows r, int kb) {
     const uint32_t k0 = (uint32_t)kb * kStageK;
+    const bool kin = kb < kblocks;       // a padding stage reads zeros, its scales too
     const uint32_t lds = lds_addr(slot_mem);
     if (d < kInstA)
-      dma16_so(rsA, lane_off + (r.a + d * inst_rows), k0,
+      dma16_so(rsA, kin ? lane_off + (r.a + d * inst_rows) : kOutOfRange, k0,
                lds + 1024u * wave + 1024u * C::kWaves * d);
     else if (d < kInstA + kInstB)
-      dma16_so(rsB, lane_off + (r.b + (d - kInstA) * inst_rows), k0,
+      dma16_so(rsB, kin ? lane_off + (r.b + (d - kInstA) * inst_rows) : kOutOfRange, k0,
                lds + C::BM * kStageK + 1024u * wave + 1024u * C::kWaves * (d - kInstA));
     else
       dma4(sc_from_a ? rsSa : rsSb,
-           (sc_lane == kOutOfRange || r.sc == kOutOfRange) ? kOutOfRange
-                                                           : sc_lane + r.sc + 4u * kb,
+           (!kin || sc_lane == kOutOfRange || r.sc == kOutOfRange) ? kOutOfRange
+                                                                    : sc_lane + r.sc + 4u * kb,
            lds + kSaOff + 256u * wave);
   };
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -907,7 +915,9 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
 
   v4f acc[RT][CT];
   v8i Bf0[CT], Bf1[CT], Alo[RH], Ahi[RH];
-  const int ns = K / kStageK;          // stages per tile: even and >= 4 (the host checks)
+  // stages per tile: K / 128 rounded up to an even count of at least 4; stages past K
+  // (the tail of a K that is not a multiple of 256) load zeros
+  const int ns = max(4, (((K + kStageK - 1) / kStageK) + 1) & ~1);
   Rows cur = rows_of(0), nxt = rows_of(1);
 
   // MFMA x of the stage (x = i CT + j) gives the block's partial sum P; fold() adds it in
@@ -1194,8 +1204,12 @@ hipError_t run_mx16(const uint8_t* A, const uint8_t* B, const float* sa, const f
       if (cost < best) { best = cost; split_m = pm; split_n = pn; }
     }
   }
-  hipLaunchKernelGGL(gemm_fp8_mx16_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
-                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  if (K % (2 * kStageK) == 0)
+    hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, false>), dim3((unsigned)grid), dim3(C::kThreads),
+                       0, s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  else
+    hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, true>), dim3((unsigned)grid), dim3(C::kThreads),
+                       0, s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   return hipGetLastError();
 }
 
@@ -1240,7 +1254,7 @@ hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const 
   // K is a multiple of 128 (checked on the host), so the step count is even
   // (the per-row B scale variant keeps two stages: four run out of registers)
   static const int forced = forced_cfg();
-  if (K % (2 * kStageK) == 0 && K >= 4 * kStageK && forced != 0)
+  if (K >= 4 * kStageK && forced != 0)
     return run_mx16b<BlkMx16<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
   const int nk = K / kBKS;
   if constexpr (BROWS != 1)
@@ -1259,11 +1273,11 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, 
     if (b_rows_per_scale == 1) return run_block<1>(A, B, sa, sb, D, m, n, k, mv, s);
     return run_block<128>(A, B, sa, sb, D, m, n, k, mv, s);
   }
-  // tensorwise: the 16x16x128 kernel where its stage plan fits (K a multiple of 256, at
-  // least 512) and the output spans at least 64 of its tiles; else the 32x32x64
-  // persistent kernel with 256x256 tiles, or 128x128 tiles for small outputs.
+  // tensorwise: the 16x16x128 kernel for K of at least 512 when the output spans at least
+  // 64 of its tiles; else the 32x32x64 persistent kernel with 256x256 tiles, or 128x128
+  // tiles for small outputs.
   // FP8LIN_GEMM_CFG (0: 256x256, 1: 128x128, 2: 16x16x128) forces a choice for sweeps.
-  const bool mx16_ok = k % (2 * kStageK) == 0 && k >= 4 * kStageK;
+  const bool mx16_ok = k >= 4 * kStageK;
   const bool big = (int64_t)M * N >= (int64_t)2048 * 2048;
   int cfg = forced_cfg();
   if (cfg < 0) cfg = big ? (mx16_ok ? 2 : 0) : 1;

@@ -87,10 +87,13 @@ def test_block_linear_step(lib, M, K, N, rv):
 
 
 @pytest.mark.parametrize("M,K,N,rv", [(2176, 768, 1152, 2176), (1408, 1024, 2304, 1350),
-                                      (1536, 768, 1280, 1500)])
+                                      (1536, 768, 1280, 1500),
+                                      # odd 128-block counts: 640 -> 5, 1152 -> 9 (padding stage)
+                                      (1280, 640, 1152, 1280)])
 def test_block_linear_step_wide_kernel(lib, M, K, N, rv):
-    """Shapes the 16x16x128 block kernel takes (contraction a multiple of 256, >= 512):
-    rows ragged against its 256-row tiles, padded token rows, all three GEMMs."""
+    """Shapes the 16x16x128 block kernel takes (contraction of at least 512): rows ragged
+    against its 256-row tiles, padded token rows, odd counts of 128-wide blocks, all three
+    GEMMs."""
     test_block_linear_step(lib, M, K, N, rv)
 
 

@@ -141,11 +141,13 @@ def test_full_size_headline_sampled(lib):
         assert abs(yh[m, n] - D) <= bound, (m, n, yh[m, n], D, bound)
 
 
-# Shapes the 16x16x128 kernel takes (output of at least 2048 x 2048, K a multiple of 256
-# and at least 512), with ragged M and N (partial 256-row / 256-column tiles) and with
-# padded rows (M_valid < M).
+# Shapes the 16x16x128 kernel takes (output of at least 2048 x 2048, K of at least 512),
+# with ragged M and N (partial 256-row / 256-column tiles), padded rows (M_valid < M), and
+# K that is not a multiple of its 256-byte stage pair (a tail chunk and a padding stage).
 @pytest.mark.parametrize("M,N,K,mv", [(2064, 2320, 512, 2064), (2320, 2064, 768, 2301),
-                                      (4096, 1040, 1024, 4000)])
+                                      (4096, 1040, 1024, 4000),
+                                      # K tails: 528 = 4 stages + 16 bytes, 1040 = 8 + 16
+                                      (2304, 2048, 528, 2300), (2048, 2176, 1040, 2048)])
 def test_wide_kernel_ragged(lib, M, N, K, mv):
     qa, sa = _codes((M, K), 31 + M, "student_t", nu=3)
     qb, sb = _codes((N, K), 32 + N, "normal", std=0.02)
