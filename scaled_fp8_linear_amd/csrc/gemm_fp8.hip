@@ -133,10 +133,8 @@ struct PCfg {
   static constexpr int kStageBytes = (BM + BN) * kBKS;
   static constexpr int kInstA = BM / (16 * kWaves), kInstB = BN / (16 * kWaves);
   static constexpr int kLoadsPerStage = kInstA + kInstB;
-  static_assert(BM % (16 * kWaves) == 0 && BN % (16 * kWaves) == 0, "dma rows");
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
   static_assert(STAGES >= 2 && STAGES <= 5, "stages");
-  static_assert(kLoadsPerStage * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(!BLOCK || (STAGES % 2 == 0 && (BROWS == 1 || BN % 128 == 0)), "block recipe");
   static_assert(!BLOCK || BROWS == 1 || WTN <= 128, "one weight scale row per wave");
 };
@@ -165,6 +163,10 @@ using IC = std::integral_constant<int, V>;
 // State and per-step work of one workgroup, shared by both kernels.
 template <class C>
 struct Tile {
+  // the 32x32x64 kernels: 16 rows per load instruction, 32x32 output tiles
+  static_assert(C::BM % (16 * C::kWaves) == 0 && C::BN % (16 * C::kWaves) == 0, "dma rows");
+  static_assert(C::WTM % 32 == 0 && C::WTN % 32 == 0, "wave tile");
+  static_assert(C::kLoadsPerStage * (C::STAGES - 2) <= 63, "vmcnt range");
   const float* sa;
   const float* sb;
   uint16_t* D;
@@ -490,9 +492,12 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   constexpr int kInstB = C::BN / (kRowsPerInst * C::kWaves);
   constexpr int kDma = kInstA + kInstB;
   constexpr int RT = C::WTM / 16, CT = C::WTN / 16;           // 16x16 tiles per wave
-  constexpr int RH = RT / 2;                                  // rows per half stage
-  constexpr int kStores = RT * CT / 2;                        // epilogue stores per lane
-  static_assert(RT % 2 == 0 && kDma <= 63 && kStores <= 63, "plan");
+  constexpr int RH = RT / 2, RS = RT - RH;                    // rows in the two halves
+  // epilogue stores per lane: one per pair of tiles, and one per row for an odd last tile
+  constexpr int kStores = RT * (CT / 2) + (CT % 2 ? RT : 0);
+  static_assert(RH >= 1 && kDma <= 63 && kStores <= 63, "plan");
+  static_assert(C::BM % (kRowsPerInst * C::kWaves) == 0 &&
+                C::BN % (kRowsPerInst * C::kWaves) == 0, "load instructions");
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[SB];
 
@@ -584,12 +589,10 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   };
 
   v4f acc[RT][CT];
-  // B fragments of this stage and the next (two sets alternate); A rows 0 .. RH-1 of
-  // the next stage are read after this stage's are used, so one set serves
   // B fragments of this stage and the next (two sets alternate); A rows 0 .. RH-1 and
   // RH .. RT-1 of this stage. Only B and A row 0 are read a stage ahead: rows 1 .. RT-1
   // are read during the stage's first half, which keeps the register peak down.
-  v8i Bf0[CT], Bf1[CT], Alo[RH], Ahi[RH];
+  v8i Bf0[CT], Bf1[CT], Alo[RH], Ahi[RS];
 
   // stages per tile: K / 128 rounded up to an even count of at least 4; stages past K
   // (the tail of a K that is not a multiple of 256) load zeros
@@ -612,7 +615,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 #pragma unroll
     for (int i = 1; i < RH; ++i) Alo[i] = rdA(mine, i);
 #pragma unroll
-    for (int i = 0; i < RH; ++i) Ahi[i] = rdA(mine, RH + i);
+    for (int i = 0; i < RS; ++i) Ahi[i] = rdA(mine, RH + i);
 #pragma unroll
     for (int i = 0; i < RH; ++i)
 #pragma unroll
@@ -636,7 +639,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     const int gs = s + 2;
     const Rows r = gs < ns ? cur : nxt;
     const int kb = gs < ns ? gs : gs - ns;
-    constexpr int kSecond = RH * CT;                 // MFMAs in the second half
+    constexpr int kSecond = RS * CT;                 // MFMAs in the second half
     constexpr int kReads = CT + 1;                   // fragments to read
 #pragma unroll
     for (int x = 0; x < kSecond; ++x) {
@@ -661,7 +664,8 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // path for every tile (a second one would have the compiler compute all 256 scaled
   // values up front for both): rows at or past M_valid are replaced by zeros, pieces
   // outside D get an offset past its end, which the range check drops.
-  static_assert(CT % 2 == 0, "tile pairs");
+  // With an odd tile count per row, the last tile goes out on its own: 8 bytes (4
+  // consecutive n) per lane.
   auto epilogue = [&](int m0, int n0) {
     const int mrow = m0 + wm * C::WTM + r16;
     const int ncol = n0 + wn * C::WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
@@ -687,6 +691,17 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
         const uint32_t off =
             in ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp : kOutOfRange;
         __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
+      }
+      if constexpr (CT % 2 != 0) {
+        constexpr int j = CT - 1;
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const int n = n0 + wn * C::WTN + 16 * j + 4 * g4;
+        v2i o = {(int)pack_bf16x2(acc[i][j][0] * si, acc[i][j][1] * si),
+                 (int)pack_bf16x2(acc[i][j][2] * si, acc[i][j][3] * si)};
+        if (!live) o = v2i{0, 0};
+        const uint32_t off =
+            (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b64(o, rsD, off, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1176,8 +1191,11 @@ using TwBig = PCfg<256, 256, 2, 4, 4, 0, 8, 0>;
 using TwBig2 = PCfg<256, 256, 2, 4, 2, 0, 8, 0>;
 using TwSmall = PCfg<128, 128, 2, 2, 4, 0, 8, 0>;
 using TwSmall2 = PCfg<128, 128, 2, 2, 2, 0, 8, 0>;
-// 16x16x128 kernel: 256x256 tiles, 4 waves of 128x128 (its own LDS plan).
+// 16x16x128 kernel: 256x256 tiles, 4 waves of 128x128 (its own LDS plan); 224-row or
+// 224-column tiles where they split the output into whole rounds of 256 tiles better.
 using TwMx16 = PCfg<256, 256, 2, 2, 2, 0, 8, 0>;
+using TwMx16M224 = PCfg<224, 256, 2, 2, 2, 0, 8, 0>;
+using TwMx16N224 = PCfg<256, 224, 2, 2, 2, 0, 8, 0>;
 // Block recipe: the partial sums need a second set of accumulators, so 256x128 tiles.
 // With one weight scale per 128 rows, 8 waves of 64x64; with a B scale per row (wgrad),
 // 8 waves of 128x32, so that a lane needs 16 B scales per 128-wide K block, not 32.
@@ -1281,7 +1299,21 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, 
   const bool big = (int64_t)M * N >= (int64_t)2048 * 2048;
   int cfg = forced_cfg();
   if (cfg < 0) cfg = big ? (mx16_ok ? 2 : 0) : 1;
-  if (cfg == 2 && mx16_ok) return run_mx16<TwMx16>(A, B, sa, sb, D, m, n, k, mv, s);
+  if (cfg == 2 && mx16_ok) {
+    // Beyond one round of 256x256 tiles, the tile shape with the shortest makespan:
+    // rounds of kMaxWorkgroups tiles times the tile's area (896 tiles of 256x256 take 4
+    // rounds, the last half empty; 1024 of 224x256 take 4 full ones, each 7/8 as long).
+    auto cost = [&](int bm, int bn) {
+      const int64_t tiles = (int64_t)((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+      return ((tiles + kMaxWorkgroups - 1) / kMaxWorkgroups) * bm * bn;
+    };
+    const int64_t c0 = cost(256, 256), cm = cost(224, 256), cn = cost(256, 224);
+    if (c0 > 256 * 256) {
+      if (cm < c0 && cm <= cn) return run_mx16<TwMx16M224>(A, B, sa, sb, D, m, n, k, mv, s);
+      if (cn < c0) return run_mx16<TwMx16N224>(A, B, sa, sb, D, m, n, k, mv, s);
+    }
+    return run_mx16<TwMx16>(A, B, sa, sb, D, m, n, k, mv, s);
+  }
   if (cfg == 1) return run_tensorwise<TwSmall, TwSmall2>(A, B, sa, sb, D, m, n, k, mv, s);
   return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, D, m, n, k, mv, s);
 }

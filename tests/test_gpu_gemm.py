@@ -161,7 +161,20 @@ def test_wide_kernel_ragged(lib, M, N, K, mv):
     assert worst < 0.25
 
 
-@pytest.mark.parametrize("M,N,K,what", [(8192, 4096, 14336, "dgrad"), (14336, 4096, 8192, "wgrad")])
+@pytest.mark.parametrize("M,N,K,mv", [
+    # more than one round of 256x256 tiles: 224-row tiles (ragged last tile row), then
+    # 224-column tiles (ragged last tile column), with a ragged contraction on each
+    (4352, 4096, 512, 4352), (4352, 4096, 528, 4301), (4096, 7152, 512, 1200),
+    (4096, 7152, 784, 900)])
+def test_narrow_tile_kernels_ragged(lib, M, N, K, mv):
+    """Output grids that the 16x16x128 kernel covers with 224x256 or 256x224 tiles (fewer
+    idle workgroups in the last round): every computed row checked against the oracle,
+    padded rows zero."""
+    test_wide_kernel_ragged(lib, M, N, K, mv)
+
+
+@pytest.mark.parametrize("M,N,K,what", [(8192, 4096, 14336, "dgrad"), (14336, 4096, 8192, "wgrad"),
+                                        (4096, 14336, 8192, "wgrad of the down projection")])
 def test_full_size_backward_shapes_sampled(lib, M, N, K, what):
     """The MLP block's dgrad (contraction over 14336) and wgrad (contraction over the 8192
     tokens) launch shapes: operands quantized on the GPU (bit-exact with the oracle, see
