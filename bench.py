@@ -13,7 +13,7 @@ N(0, 0.02), output gradients N(0, 1e-3). Timing: W untimed warm-up steps
 synchronizations; HIP events around every kernel call give per-launch
 durations for the roofline figures.
 
-Prints ONE JSON line. ``--gpus N`` with N > 1 exits: this build measures one GPU.
+Prints ONE JSON line. ``--gpus N`` with N > 1 exits: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -44,6 +44,8 @@ def _parse():
                     help="skip the block-recipe and packed-varlen measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 512 MiB buffer three times (for scaling HBM byte counters)")
+    ap.add_argument("--data-sensitivity", action="store_true",
+                    help="only time the 8192x4096x14336 GEMM on random, constant and zero codes")
     return ap.parse_args()
 
 
@@ -61,14 +63,70 @@ def copy_calibration():
                                            "bytes_written_per_copy": nbytes, "copies": 3}}))
 
 
+def data_sensitivity(launches=20):
+    """The same GEMM launch (M=8192, N=4096, K=14336) on three sets of operand codes: codes
+    of normal data (as in the step), all codes 0x38 (1.0) and all codes 0. The instruction
+    stream and memory traffic are identical; only the bits the matrix cores and data paths
+    toggle differ, so a gap in time is a gap in clock (the chip's power limit)."""
+    import torch
+    import scaled_fp8_linear_amd as m
+    m.load()
+    dev = torch.device("cuda:0")
+    M, N, K = 8192, 4096, 14336
+    gen = torch.Generator(device=dev).manual_seed(0)
+    one = torch.ones(1, device=dev)
+    res = {}
+    for name in ("normal", "constant_1.0", "zeros", "normal_again"):
+        if name.startswith("normal"):
+            xa = torch.randn(M, K, device=dev, generator=gen).to(torch.bfloat16)
+            xb = (torch.randn(N, K, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+            qa = m.fp8_quantize_amax(xa, scale_inv=448.0 / xa.abs().max().float().reshape(1),
+                                     want_q_t=False)[0]
+            qb = m.fp8_quantize_amax(xb, scale_inv=448.0 / xb.abs().max().float().reshape(1),
+                                     want_q_t=False)[0]
+            del xa, xb
+        else:
+            code = 0x38 if name.startswith("constant") else 0
+            qa = torch.full((M, K), code, dtype=torch.uint8, device=dev)
+            qb = torch.full((N, K), code, dtype=torch.uint8, device=dev)
+        y = m.fp8_linear_fwd(qa, qb, one, one)
+        for _ in range(3):
+            m.fp8_linear_fwd(qa, qb, one, one, y=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            m.fp8_linear_fwd(qa, qb, one, one, y=y)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        res[name] = {"us_per_launch": round(us, 1), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
+        print(json.dumps({"data_sensitivity": name, **res[name]}), flush=True)
+    print(json.dumps({"data_sensitivity": res, "shape": [M, N, K], "launches": launches}))
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mlp_8192x4096x14336.txt")
+
+
+def source_digest(paths):
+    """sha256 (first 16 hex digits) of C/HIP sources with comments and blank lines removed,
+    so that an edit of comments alone keeps the digest while any change of code alters it."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in paths:
+        text = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(kernel: str):
     """HBM bytes per launch of ``kernel`` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary, scaled by the copy calibration; None when the summary is missing or the kernel's
-    sources have changed since the counters were taken."""
-    import hashlib
+    code (its sources without comments) has changed since the counters were taken."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
@@ -81,13 +139,11 @@ def counter_traffic(kernel: str):
                 kv[k] = v.strip()
         if kv.get("kernel") != kernel:
             continue
-        h = hashlib.sha256()
-        for f in kv["sources"].split():
-            try:
-                h.update(open(os.path.join(ROOT, f), "rb").read())
-            except OSError:
-                return None
-        if h.hexdigest()[:16] != kv["source_sha256"]:
+        try:
+            digest = source_digest(kv["sources"].split())
+        except OSError:
+            return None
+        if digest != kv["code_sha256"]:
             return None
         rd = float(kv["fetch_kib_mean"]) * float(kv["fetch_factor"]) * 1024
         wr = float(kv["write_kib_mean"]) * float(kv["write_factor"]) * 1024
@@ -291,12 +347,15 @@ def measure_varlen(torch, m, workloads, steps, warmup):
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build measures one GPU: the hot path runs on one "
+        print(json.dumps({"error": "bench.py measures one GPU: the hot path runs on one "
                                    "device and has no cross-GPU step; run with --gpus 1"}))
         sys.exit(2)
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.data_sensitivity:
+        data_sensitivity()
         return
 
     import torch

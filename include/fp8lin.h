@@ -49,7 +49,7 @@ typedef enum fp8_status {
   FP8_ERR_NULL = 1,        /* a required pointer is NULL                     */
   FP8_ERR_SHAPE = 2,       /* a size is negative, not a multiple of 16, ... */
   FP8_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned              */
-  FP8_ERR_UNSUPPORTED = 4, /* valid request this build does not implement   */
+  FP8_ERR_UNSUPPORTED = 4, /* valid request the library does not implement  */
   FP8_ERR_HIP = 5          /* a HIP launch or runtime call failed           */
 } fp8_status;
 

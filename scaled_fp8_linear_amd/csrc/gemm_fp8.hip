@@ -472,20 +472,20 @@ gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict
 constexpr int kStageK = 128;   // K bytes per LDS stage of gemm_fp8_mx16_kernel
 
 // ---------------------------------------------------------------------------
-// 16x16x128 kernel (tensorwise scaling): 256x256 tiles, 4 waves of 128x128, each wave
-// an 8x8 grid of v_mfma_f32_16x16x128_f8f6f4 tiles (the 16x16 form keeps the matrix
-// cores busier than 32x32x64 when LDS reads run alongside, and moves half as many
-// accumulator bytes per FLOP). An LDS stage holds 128 K bytes of the tile's 256 A and
-// 256 B rows (64 KB), in two slots, loaded straight to LDS: a 64-byte K step would
-// fetch each 128-byte line in two halves, one step apart, which halves the L2 -> CU
-// throughput. One MFMA covers a whole stage's K, so per stage a wave runs
-// 64 MFMAs (rows i = 0..7 of 16x16 tiles, all 8 columns j each):
-//   first half  (rows 0..3): A fragments of rows 4..7 are read in between;
+// 16x16x128 kernel (tensorwise scaling): 256x256 tiles (or 224x256 / 256x224), 4 waves
+// of 128x128 (112x128 / 128x112), each wave an RT x CT grid of v_mfma_f32_16x16x128_f8f6f4
+// tiles (the 16x16 form keeps the matrix cores busier than 32x32x64 when LDS reads run
+// alongside, and moves half as many accumulator bytes per FLOP). An LDS stage holds 128
+// K bytes of the tile's A and B rows (64 KB at 256x256), in two slots, loaded straight
+// to LDS: a 64-byte K step would fetch each 128-byte line in two halves, one step apart,
+// which halves the L2 -> CU throughput. One MFMA covers a whole stage's K, so per stage
+// a wave runs RT x CT MFMAs (rows i of 16x16 tiles, all CT columns j each):
+//   first half  (rows 0 .. RT/2-1): A fragments of rows 1 .. RT-1 are read in between;
 //   mid-stage:  the wave waits for its loads of stage s + 1; a barrier publishes them
 //               and frees this stage's slot (all its reads are done by then);
-//   second half (rows 4..7): the loads of stage s + 2 go into this slot, and stage
-//               s + 1's B fragments and rows 0..3 of its A fragments are read.
-// B fragments of a stage stay in registers for all 64 MFMAs (two sets alternate).
+//   second half (the other rows): the loads of stage s + 2 go into this slot, and stage
+//               s + 1's B fragments and A row 0 are read.
+// B fragments of a stage stay in registers for all its MFMAs (two sets alternate).
 // Fragment of a 16-row tile: lane l holds 32 bytes of row l % 16 at K offset
 // 32 (l / 16); the instruction pairs A and B by lane and byte, so this K order is as
 // good as any. The B tile goes in as the first operand, so a lane's 4 results are 4
