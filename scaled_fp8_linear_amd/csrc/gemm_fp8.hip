@@ -91,6 +91,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // right for groups of 16 consecutive lanes, costs a second cycle per read here).
 __device__ __forceinline__ int row_swizzle(int r) { return (r >> 1) & 5; }
 
+// 16-byte LDS read at an LDS byte address (a base register plus a constant folds into the
+// instruction's offset field)
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(3))) v4u lds_v4u;
+__device__ __forceinline__ v4u lds16(uint32_t a) { return *(lds_v4u*)(uintptr_t)a; }
+
 // One 16-byte-per-lane buffer load written straight to LDS at lds + 16 * lane. Issued
 // through inline asm so that the compiler does not guard later LDS reads of other
 // stages with waits on it; the kernels wait for these loads themselves (vmcnt) before
@@ -776,7 +782,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 //                       per 128 B rows, the single value at p = BM.
 // Every wave issues the same loads per stage (lanes with nothing to load read out of
 // range), so the memory counts stay uniform.
-template <class C>
+template <class C, bool PAD>
 __global__ void __launch_bounds__(C::kThreads, 1)
 gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                       const float* __restrict__ sa, const float* __restrict__ sb,
@@ -884,7 +890,8 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   // inside a row, in the SGPR operand
   auto dma = [&](int d, uint8_t* slot_mem, Rows r, int kb) {
     const uint32_t k0 = (uint32_t)kb * kStageK;
-    const bool kin = kb < kblocks;       // a padding stage reads zeros, its scales too
+    // PAD (an odd count of K blocks): the padding stage reads zeros, its scales too
+    const bool kin = !PAD || kb < kblocks;
     const uint32_t lds = lds_addr(slot_mem);
     if (d < kInstA)
       dma16_so(rsA, kin ? lane_off + (r.a + d * inst_rows) : kOutOfRange, k0,
@@ -900,39 +907,66 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   };
   const int r16 = lane & 15, g4 = lane >> 4;
   const int sw = row_swizzle(r16);
-  const uint32_t fo0 = r16 * kStageK + 16 * ((2 * g4) ^ sw);
-  const uint32_t fo1 = r16 * kStageK + 16 * ((2 * g4 + 1) ^ sw);
-  auto rd = [&](const uint8_t* q) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(q + fo0);
-    const uint4 hi = *reinterpret_cast<const uint4*>(q + fo1);
+  // the lane's two 16-byte pieces of its fragment row, as offsets into a slot, with the
+  // wave's first A row and first B row folded in: a read then adds the slot's base (one
+  // add per slot and stage) and a constant that fits the instruction's offset field
+  const uint32_t fa0 = (uint32_t)(wm * C::WTM + r16) * kStageK + 16 * ((2 * g4) ^ sw);
+  const uint32_t fa1 = (uint32_t)(wm * C::WTM + r16) * kStageK + 16 * ((2 * g4 + 1) ^ sw);
+  const uint32_t fb0 = fa0 + (uint32_t)(C::BM + wn * C::WTN - wm * C::WTM) * kStageK;
+  const uint32_t fb1 = fa1 + (uint32_t)(C::BM + wn * C::WTN - wm * C::WTM) * kStageK;
+  static_assert((C::BM + C::BN) * kStageK < 65536, "row offsets fit the LDS offset field");
+  auto rd = [&](uint32_t lo_at, uint32_t hi_at) {
+    const v4u lo = lds16(lo_at);
+    const v4u hi = lds16(hi_at);
     v8i v;
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
     return v;
   };
-  auto rdA = [&](const uint8_t* sm, int i) { return rd(sm + (wm * C::WTM + 16 * i) * kStageK); };
-  auto rdB = [&](const uint8_t* sm, int j) {
-    return rd(sm + (C::BM + wn * C::WTN + 16 * j) * kStageK);
+  // a slot's read bases (computed once per stage, opaque to the compiler, so that each
+  // read is base + constant and the constant goes in the offset field)
+  struct Bases { uint32_t a0, a1, b0, b1; };
+  auto slot_addr = [&](const uint8_t* sm) {   // the slot's LDS address, one SGPR
+    uint32_t b = lds_addr(sm);
+    asm volatile("" : "+s"(b));
+    return b;
+  };
+  auto bases = [&](const uint8_t* sm) {
+    const uint32_t b = slot_addr(sm);
+    Bases r{b + fa0, b + fa1, b + fb0, b + fb1};
+    asm volatile("" : "+v"(r.a0), "+v"(r.a1), "+v"(r.b0), "+v"(r.b1));
+    return r;
+  };
+  auto rdA = [&](const Bases& q, int i) {
+    return rd(q.a0 + 16u * i * kStageK, q.a1 + 16u * i * kStageK);
+  };
+  auto rdB = [&](const Bases& q, int j) {
+    return rd(q.b0 + 16u * j * kStageK, q.b1 + 16u * j * kStageK);
   };
   // this stage's scales: fa[i] = sa of the lane's row in tile row i (times sb when B has one
   // scale per tile), fb the lane's column scales when B has one per row
   float fa[RT];
   float fb[BROWS == 1 ? CT * 4 : 1];
+  const uint32_t fsa = kSaOff + 4u * (uint32_t)(wm * C::WTM + r16 * RT);
+  const uint32_t fsb = kSbOff + 4u * (uint32_t)(wn * C::WTN + g4 * 4 * CT);
   auto rd_scales = [&](const uint8_t* sm) {
     static_assert(RT % 4 == 0, "row scales by 16 bytes");
-    const float4* qa = reinterpret_cast<const float4*>(sm + kSaOff + 4 * (wm * C::WTM + r16 * RT));
+    uint32_t ba = slot_addr(sm) + fsa;
+    asm volatile("" : "+v"(ba));
 #pragma unroll
     for (int v = 0; v < RT / 4; ++v) {
-      const float4 a4 = qa[v];
-      fa[4 * v + 0] = a4.x; fa[4 * v + 1] = a4.y; fa[4 * v + 2] = a4.z; fa[4 * v + 3] = a4.w;
+      const v4u a4 = lds16(ba + 16u * v);
+      fa[4 * v + 0] = __uint_as_float(a4.x); fa[4 * v + 1] = __uint_as_float(a4.y);
+      fa[4 * v + 2] = __uint_as_float(a4.z); fa[4 * v + 3] = __uint_as_float(a4.w);
     }
     if constexpr (BROWS == 1) {
-      const float4* qb =
-          reinterpret_cast<const float4*>(sm + kSbOff + 4 * (wn * C::WTN + g4 * 4 * CT));
+      uint32_t bb = slot_addr(sm) + fsb;
+      asm volatile("" : "+v"(bb));
 #pragma unroll
       for (int j = 0; j < CT; ++j) {
-        const float4 b4 = qb[j];
-        fb[4 * j + 0] = b4.x; fb[4 * j + 1] = b4.y; fb[4 * j + 2] = b4.z; fb[4 * j + 3] = b4.w;
+        const v4u b4 = lds16(bb + 16u * j);
+        fb[4 * j + 0] = __uint_as_float(b4.x); fb[4 * j + 1] = __uint_as_float(b4.y);
+        fb[4 * j + 2] = __uint_as_float(b4.z); fb[4 * j + 3] = __uint_as_float(b4.w);
       }
     } else {
       fb[0] = *reinterpret_cast<const float*>(sm + kSbOff);
@@ -947,7 +981,10 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   Rows cur = rows_of(0), nxt = rows_of(1);
 
   // MFMA x of the stage (x = i CT + j) gives the block's partial sum P; fold() adds it in
-  // with its scale. Software-pipelined: MFMA x is issued before the fold of MFMA x - 1.
+  // with its scale. Software-pipelined: MFMA x is issued before the fold of MFMA x - L,
+  // L = 2 where registers allow (with L = 1 the fold waits on the matrix core's result;
+  // the kernel with a scale per B row holds 16 more scales and keeps L = 1).
+  constexpr int L = BROWS == 1 ? 1 : 2;
   auto mfma_x = [&](int x, const v8i* Bc) {
     const int i = x / CT, j = x % CT;
     const v4f z = {};
@@ -971,20 +1008,22 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
     constexpr bool LAST = decltype(LAST_)::value != 0;
     constexpr bool FIRST = decltype(FIRST_)::value != 0;
     constexpr int kHalf = RH * CT;       // MFMAs per half stage
-    v4f P[2];
+    static_assert(kHalf >= L, "fold lag");
+    v4f P[L + 1];
     // first half: rows 0 .. RH-1; this stage's scales, then A rows RH .. RT-1, are read
+    const Bases qm = bases(mine);
     rd_scales(mine);
 #pragma unroll
-    for (int i = 0; i < RH; ++i) Ahi[i] = rdA(mine, RH + i);
+    for (int i = 0; i < RH; ++i) Ahi[i] = rdA(qm, RH + i);
     if constexpr (BROWS != 1) {
 #pragma unroll
       for (int i = 0; i < RT; ++i) fa[i] *= fb[0];
     }
 #pragma unroll
     for (int x = 0; x < kHalf; ++x) {
-      P[x & 1] = mfma_x(x, Bc);
+      P[x % (L + 1)] = mfma_x(x, Bc);
       __builtin_amdgcn_sched_barrier(0);
-      if (x > 0) fold(FIRST_, x - 1, P[(x - 1) & 1]);
+      if (x >= L) fold(FIRST_, x - L, P[(x - L) % (L + 1)]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // own loads of stage s + 1 landed (those of stage s + 2, and after a previous tile
@@ -1000,24 +1039,27 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
     const Rows r = gs < ns ? cur : nxt;
     const int kb = gs < ns ? gs : gs - ns;
     constexpr int kReads = CT + RH;
+    Bases qo{};
+    if constexpr (!LAST) qo = bases(other);
 #pragma unroll
     for (int y = 0; y < kHalf; ++y) {
       const int x = kHalf + y;
-      P[x & 1] = mfma_x(x, Bc);
+      P[x % (L + 1)] = mfma_x(x, Bc);
       __builtin_amdgcn_sched_barrier(0);
-      fold(FIRST_, x - 1, P[(x - 1) & 1]);
+      fold(FIRST_, x - L, P[(x - L) % (L + 1)]);
 #pragma unroll
       for (int d = y * kDma / kHalf; d < (y + 1) * kDma / kHalf; ++d) dma(d, mine, r, kb);
 #pragma unroll
       for (int f = y * kReads / kHalf; f < (y + 1) * kReads / kHalf; ++f) {
         if constexpr (!LAST) {
-          if (f < CT) Bn[f] = rdB(other, f);
-          else Alo[f - CT] = rdA(other, f - CT);
+          if (f < CT) Bn[f] = rdB(qo, f);
+          else Alo[f - CT] = rdA(qo, f - CT);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    fold(FIRST_, 2 * kHalf - 1, P[(2 * kHalf - 1) & 1]);
+#pragma unroll
+    for (int x = 2 * kHalf - L; x < 2 * kHalf; ++x) fold(FIRST_, x, P[x % (L + 1)]);
   };
 
   // epilogue: as gemm_fp8_mx16_kernel's (the block scales are already applied)
@@ -1063,11 +1105,11 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   asm volatile("" ::: "memory");
   int g = 0;                           // global index of the tile's first stage
   auto first_frags = [&]() {
-    uint8_t* sm = slot_of(g);
+    const Bases q = bases(slot_of(g));
 #pragma unroll
-    for (int j = 0; j < CT; ++j) Bf0[j] = rdB(sm, j);
+    for (int j = 0; j < CT; ++j) Bf0[j] = rdB(q, j);
 #pragma unroll
-    for (int i = 0; i < RH; ++i) Alo[i] = rdA(sm, i);
+    for (int i = 0; i < RH; ++i) Alo[i] = rdA(q, i);
   };
   first_frags();
   for (int ti = 0; ti < count; ++ti) {
@@ -1269,8 +1311,15 @@ hipError_t run_mx16b(const uint8_t* A, const uint8_t* B, const float* sa, const 
       if (cost < best) { best = cost; split_m = pm; split_n = pn; }
     }
   }
-  hipLaunchKernelGGL(gemm_fp8_mx16b_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
-                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  // an odd count of K blocks ends each tile with a padding stage (stages come in pairs)
+  if ((K / kStageK) % 2 == 0)
+    hipLaunchKernelGGL((gemm_fp8_mx16b_kernel<C, false>), dim3((unsigned)grid), dim3(C::kThreads),
+                       0, s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m,
+                       split_n);
+  else
+    hipLaunchKernelGGL((gemm_fp8_mx16b_kernel<C, true>), dim3((unsigned)grid), dim3(C::kThreads),
+                       0, s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m,
+                       split_n);
   return hipGetLastError();
 }
 

@@ -27,9 +27,22 @@ def test_digest_changes_with_code(tmp_path):
     assert bench.source_digest([a]) != bench.source_digest([b])
 
 
-def test_committed_traffic_matches_current_code():
-    """The committed counter summary was taken on the code that is in the tree."""
-    t = bench.counter_traffic("gemm_fp8_mx16_kernel")
-    q = bench.counter_traffic("quantize_tensorwise_kernel")
-    assert t is not None and t["bytes"] > 0
-    assert q is not None and q["bytes"] > 0
+def test_committed_traffic_is_used_only_for_its_code(tmp_path, monkeypatch):
+    """A summary whose digest matches the sources gives its bytes; a stale one gives None."""
+    src = _write(tmp_path, "k.hip", "__global__ void k() {}\n")
+    good = bench.source_digest([src])
+
+    def summary(digest):
+        f = tmp_path / f"traffic_{digest}.txt"
+        f.write_text(f"# header\nkernel k\nsources {src}\ncode_sha256 {digest}\n"
+                     "fetch_kib_mean 100.0\nwrite_kib_mean 50.0\n"
+                     "fetch_factor 2.0\nwrite_factor 1.0\n")
+        return str(f)
+
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", summary(good))
+    t = bench.counter_traffic("k")
+    assert t == {"bytes": 200 * 1024 + 50 * 1024, "read_bytes": 200 * 1024,
+                 "write_bytes": 50 * 1024}
+    assert bench.counter_traffic("other") is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", summary("0" * 16))
+    assert bench.counter_traffic("k") is None
