@@ -160,7 +160,9 @@ int fp8_scale_update(int mode, const float* amax, float* hist, int32_t len, int3
  *   FP8_BLOCK_1x128 (the block recipe): sx [M, K/128], sw [N/128, K/128];
  *       the scales multiply each 128-wide partial sum.
  *   M, N, K multiples of 16 (K, N multiples of 128 in the block recipe);
- *   0 <= M_valid <= M.
+ *   0 <= M_valid <= M. K = 0 (an empty sum) writes +0 everywhere and reads
+ *   neither operands nor scales, which may then be NULL (the same holds for
+ *   the contraction size of dgrad and wgrad).
  */
 int fp8_linear_fwd(const void* qx, const void* qw, const float* sx, const float* sw, void* y,
                    int64_t M, int64_t N, int64_t K, int64_t M_valid, int gran, void* stream);
@@ -188,7 +190,8 @@ int fp8_linear_dgrad(const void* qg, const void* qw_t, const float* sg, const fl
  *
  *   qg_t e4m3 [N, M], qx_t e4m3 [K, M] (q_t outputs of quantizing g and x).
  *   dw   bf16 [N, K]: dw[n,k] = bf16_rne(sg * sx * sum_m qg_t[n,m] * qx_t[k,m]).
- *        Padded tokens contribute nothing because their codes are 0x00.
+ *        Padded tokens contribute nothing because their codes are 0x00; with
+ *        M = 0 (no tokens) dw is all +0.
  *   FP8_TENSORWISE: sg, sx float32 [1] -- sx must be the scale that
  *        quantized x in the forward (not the updated one).
  *   FP8_BLOCK_1x128: sg = g's scale_t [N, M/128], sx = x's scale_t [K, M/128].

@@ -63,8 +63,10 @@ int check_gemm(const char* fn, const void* a, const void* b, const float* s1, co
   if (kc >= kMaxContraction)
     return fail(FP8_ERR_UNSUPPORTED, "%s: contraction size %lld >= 2^17", fn, (long long)kc);
   if (rows_a * rows_b > 0) {
-    if (!d || !s1 || !s2) return fail(FP8_ERR_NULL, "%s: NULL output or scale pointer", fn);
-    if (kc > 0 && (!a || !b)) return fail(FP8_ERR_NULL, "%s: NULL operand", fn);
+    if (!d) return fail(FP8_ERR_NULL, "%s: NULL output", fn);
+    // an empty contraction reads neither operands nor scales (the output is all zeros)
+    if (kc > 0 && (!a || !b || !s1 || !s2))
+      return fail(FP8_ERR_NULL, "%s: NULL operand or scale pointer", fn);
     if (!aligned16(a) || !aligned16(b) || !aligned16(d))
       return fail(FP8_ERR_ALIGN, "%s: operands and output must be 16-byte aligned", fn);
   }

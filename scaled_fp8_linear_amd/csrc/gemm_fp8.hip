@@ -1346,6 +1346,8 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, 
                            uint16_t* D, int64_t M, int64_t N, int64_t K, int64_t M_valid,
                            bool block_scaled, int b_rows_per_scale, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  // an empty contraction (e.g. a weight gradient over no tokens): every sum is +0
+  if (K == 0) return launch_fill_u32(reinterpret_cast<uint32_t*>(D), 0u, M * N / 2, s);
   const int m = (int)M, n = (int)N, k = (int)K, mv = (int)M_valid;
   if (block_scaled) {
     if (b_rows_per_scale == 1) return run_block<1>(A, B, sa, sb, D, m, n, k, mv, s);

@@ -61,6 +61,8 @@ def test_gemm_argument_checks(lib):
     assert lib.fp8_linear_fwd(p, p, p, p, p, 16, 16, 1 << 17, 16, 0, None) == 4      # K too long
     assert lib.fp8_linear_dgrad(p, p, p, p, p, 16, 16, -16, 16, 0, None) == 2
     assert lib.fp8_linear_fwd(p, p, p, p, p, 16, 16, 48, 16, 1, None) == 2           # block K%128
+    assert lib.fp8_linear_fwd(p, p, None, p, p, 16, 16, 16, 16, 0, None) == 1        # NULL sx
+    assert lib.fp8_linear_wgrad(p, p, p, None, p, 16, 16, 16, 0, None) == 1          # NULL sx
 
 
 def test_quantize_argument_checks(lib):

@@ -112,6 +112,49 @@ def test_special_operands(lib):
     assert np.all(host_bf16_f64(y)[:, 5] == 0)
 
 
+def test_degenerate_shapes(lib):
+    """No tokens, an empty contraction (every sum is +0, operands and scales unread), and no
+    valid rows, on the small-output kernel and on the 16x16x128 kernel."""
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    one = dev_f32(1.0)
+    note("fp8_linear_fwd with M = 0")
+    qb, sb = _codes((128, 128), 61, std=1.0)
+    y = lib.fp8_linear_fwd(torch.empty((0, 128), **u8), _dev(qb), one, dev_f32(sb))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 128)
+    for N, K in [(128, 64), (2048, 2048)]:
+        for gran in (lib.FP8_TENSORWISE, lib.FP8_BLOCK_1x128):
+            note(f"fp8_linear_wgrad over 0 tokens N={N} K={K} gran={gran}")
+            dw = torch.full((N, K), 3.0, dtype=torch.bfloat16, device="cuda")
+            if gran == lib.FP8_TENSORWISE:
+                sg, sx = one, one
+            else:
+                sg = torch.empty((N, 0), dtype=torch.float32, device="cuda")
+                sx = torch.empty((K, 0), dtype=torch.float32, device="cuda")
+            lib.fp8_linear_wgrad(torch.empty((N, 0), **u8), torch.empty((K, 0), **u8), sg, sx,
+                                 dw=dw, gran=gran)
+            torch.cuda.synchronize()
+            assert torch.all(dw.view(torch.int16) == 0), (N, K, gran)
+    for M, N, K in [(64, 128, 128), (2048, 2048, 512)]:
+        note(f"fp8_linear_fwd with M_valid = 0, M={M} N={N} K={K}")
+        qa = np.full((M, K), 0x7F, np.uint8)          # NaN codes: still zeros
+        qb, sb = _codes((N, K), 62 + N, std=1.0)
+        y = torch.full((M, N), 3.0, dtype=torch.bfloat16, device="cuda")
+        lib.fp8_linear_fwd(_dev(qa), _dev(qb), one, dev_f32(sb), y=y, M_valid=0)
+        torch.cuda.synchronize()
+        assert torch.all(y.view(torch.int16) == 0), (M, N, K)
+    note("block recipe fwd with M_valid = 0")
+    M, N, K = 256, 384, 512
+    qa = np.full((M, K), 0x7F, np.uint8)
+    qb, _ = _codes((N, K), 63, std=1.0)
+    sa = torch.ones((M, K // 128), dtype=torch.float32, device="cuda")
+    sw = torch.ones((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.full((M, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    lib.fp8_linear_fwd(_dev(qa), _dev(qb), sa, sw, y=y, M_valid=0, gran=lib.FP8_BLOCK_1x128)
+    torch.cuda.synchronize()
+    assert torch.all(y.view(torch.int16) == 0)
+
+
 def test_full_size_headline_sampled(lib):
     """The MLP block's gate/up forward at M=8192, K=4096, N=14336 (the launch configuration the
     benchmark times): 2048 sampled outputs computed one by one by the oracle."""
