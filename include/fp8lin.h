@@ -68,6 +68,22 @@ typedef enum fp8_scale_mode {
 } fp8_scale_mode;
 
 /*
+ * Flags OR-ed into fp8_quantize_amax's gran / fp8_scale_update's mode. A
+ * delayed-scaling step consumes each amax exactly once, so the update that
+ * reads it can also clear it, and the next quantize pass can fold its max
+ * into the cleared value instead of zeroing it first (one launch less per
+ * quantized tensor).
+ */
+enum {
+  FP8_AMAX_ACCUMULATE = 0x100, /* fp8_quantize_amax, TENSORWISE only: amax[0]
+                                  = max(amax[0], max|x|) instead of being
+                                  overwritten; amax[0] must hold a
+                                  non-negative float32 (or NaN) on entry  */
+  FP8_SCALE_CLEAR_AMAX = 0x100 /* fp8_scale_update, FROM_AMAX and RECORD:
+                                  after amax[0] is read it is set to +0   */
+};
+
+/*
  * fp8_quantize_amax -- fused bf16 -> e4m3 quantize with its amax, emitting
  * the row-major codes and their transpose in one pass over x.
  *
@@ -93,7 +109,8 @@ typedef enum fp8_scale_mode {
  *   q_t        e4m3 [cols, rows] or NULL: q_t[c,r] = q[r,c].
  *   amax       float32 [1] or NULL: OVERWRITTEN with max |x[r,c]| over the
  *              valid rows (exact; 0 for empty input; NaN if a valid element is
- *              NaN). Computed on the same pass.
+ *              NaN). Computed on the same pass. With FP8_AMAX_ACCUMULATE in
+ *              gran it becomes max(amax[0], that maximum) instead.
  *   scale, scale_t  must be NULL.
  *
  * FP8_BLOCK_1x128 (activations, gradients; current per-tile scaling):
@@ -139,11 +156,13 @@ int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_va
  *   scale[0] = m / 448, scale_inv[0] = 448 / m; otherwise both are left as
  *   they were. amax and pos are ignored. The ring starts as all ones and the
  *   caller refreshes when its step counter reaches a multiple of 16.
+ * FP8_SCALE_CLEAR_AMAX (flag, FROM_AMAX and RECORD): amax[0] is set to +0
+ *   after it is read, ready for a FP8_AMAX_ACCUMULATE quantize pass.
  *
  * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE (len < 1, pos out of range, bad mode
  * -> FP8_ERR_UNSUPPORTED), FP8_ERR_HIP.
  */
-int fp8_scale_update(int mode, const float* amax, float* hist, int32_t len, int32_t pos,
+int fp8_scale_update(int mode, float* amax, float* hist, int32_t len, int32_t pos,
                      float* scale, float* scale_inv, void* stream);
 
 /*

@@ -6,8 +6,9 @@ declared in ``include/fp8lin.h``); this package is its thin Python binding
 used for device memory and streams only. Importing works without the built
 library; calling any entry point without it raises.
 """
-from ._abi import (FP8_BLOCK_1x128, FP8_BLOCK_128x128, FP8_SCALE_FROM_AMAX, FP8_SCALE_RECORD,
-                   FP8_SCALE_REFRESH, FP8_TENSORWISE, Fp8Error, Slot, fp8_last_error,
+from ._abi import (FP8_AMAX_ACCUMULATE, FP8_BLOCK_1x128, FP8_BLOCK_128x128, FP8_SCALE_CLEAR_AMAX,
+                   FP8_SCALE_FROM_AMAX, FP8_SCALE_RECORD, FP8_SCALE_REFRESH, FP8_TENSORWISE,
+                   Fp8Error, Slot, fp8_last_error,
                    fp8_linear_dgrad, fp8_linear_fwd, fp8_linear_wgrad, fp8_pad_tokens,
                    fp8_quantize_amax, fp8_scale_update, fp8_version, load)
 from .state import DelayedScalingLinear
@@ -15,4 +16,5 @@ from .state import DelayedScalingLinear
 __all__ = ["fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
            "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version", "load",
            "Fp8Error", "Slot", "DelayedScalingLinear", "FP8_TENSORWISE", "FP8_BLOCK_1x128",
-           "FP8_BLOCK_128x128", "FP8_SCALE_FROM_AMAX", "FP8_SCALE_RECORD", "FP8_SCALE_REFRESH"]
+           "FP8_BLOCK_128x128", "FP8_SCALE_FROM_AMAX", "FP8_SCALE_RECORD", "FP8_SCALE_REFRESH",
+           "FP8_AMAX_ACCUMULATE", "FP8_SCALE_CLEAR_AMAX"]

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8lin.s
 FP8_OK, FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = range(6)
 FP8_TENSORWISE, FP8_BLOCK_1x128, FP8_BLOCK_128x128 = 0, 1, 2
 FP8_SCALE_FROM_AMAX, FP8_SCALE_RECORD, FP8_SCALE_REFRESH = 0, 1, 2
+FP8_AMAX_ACCUMULATE = 0x100     # flag for fp8_quantize_amax (tensorwise)
+FP8_SCALE_CLEAR_AMAX = 0x100    # flag for fp8_scale_update (FROM_AMAX, RECORD)
 
 EXPORTS = ("fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
            "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version")
@@ -128,11 +130,15 @@ def _fptr(v, name):
 
 def fp8_quantize_amax(x, rows_valid=None, gran=FP8_TENSORWISE, scale_inv=None, q=None, q_t=None,
                       amax=None, scale=None, scale_t=None, want_q=True, want_q_t=True,
-                      want_amax=True, stream=None):
+                      want_amax=True, amax_accumulate=False, stream=None):
     """Quantize a bf16 [rows, cols] tensor. Returns (q, q_t, amax, scale, scale_t).
 
     Outputs that are not passed in are allocated here (``want_*`` False skips them).
+    ``amax_accumulate`` (tensorwise): fold max|x| into the given ``amax`` instead of
+    overwriting it.
     """
+    if amax_accumulate and amax is None:
+        raise ValueError("amax_accumulate needs the amax tensor to fold into")
     _bf16(x)
     rows, cols = x.shape
     rv = rows if rows_valid is None else int(rows_valid)
@@ -157,16 +163,19 @@ def fp8_quantize_amax(x, rows_valid=None, gran=FP8_TENSORWISE, scale_inv=None, q
                                   dtype=torch.float32, device=dev)
     q, q_t = _codes(q), _codes(q_t)
     _check("fp8_quantize_amax", load().fp8_quantize_amax(
-        _ptr(x), rows, cols, rv, gran, _fptr(scale_inv, "scale_inv"), _ptr(q), _ptr(q_t),
+        _ptr(x), rows, cols, rv, gran | (FP8_AMAX_ACCUMULATE if amax_accumulate else 0),
+        _fptr(scale_inv, "scale_inv"), _ptr(q), _ptr(q_t),
         _fptr(amax, "amax"), _fptr(scale, "scale"), _fptr(scale_t, "scale_t"), _stream(stream)))
     return q, q_t, amax, scale, scale_t
 
 
-def fp8_scale_update(mode, amax=None, hist=None, pos=0, scale=None, scale_inv=None, stream=None):
-    """One scale bookkeeping op on the device (see fp8lin.h for the modes)."""
+def fp8_scale_update(mode, amax=None, hist=None, pos=0, scale=None, scale_inv=None,
+                     clear_amax=False, stream=None):
+    """One scale bookkeeping op on the device (see fp8lin.h for the modes).
+    ``clear_amax``: set amax to +0 after reading it (FROM_AMAX, RECORD)."""
     length = 0 if hist is None else hist.numel()
     _check("fp8_scale_update", load().fp8_scale_update(
-        int(mode), _fptr(amax, "amax"), _fptr(hist, "hist"), length, int(pos),
+        int(mode) | (FP8_SCALE_CLEAR_AMAX if clear_amax else 0), _fptr(amax, "amax"), _fptr(hist, "hist"), length, int(pos),
         _fptr(scale, "scale"), _fptr(scale_inv, "scale_inv"), _stream(stream)))
 
 

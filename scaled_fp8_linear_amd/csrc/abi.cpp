@@ -85,6 +85,10 @@ int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_va
                       const float* scale_inv, void* q, void* q_t, float* amax, float* scale,
                       float* scale_t, void* stream) {
   const char* fn = "fp8_quantize_amax";
+  const bool accumulate = (gran & FP8_AMAX_ACCUMULATE) != 0;
+  gran &= ~FP8_AMAX_ACCUMULATE;
+  if (accumulate && gran != FP8_TENSORWISE)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: FP8_AMAX_ACCUMULATE is for FP8_TENSORWISE", fn);
   if (rows < 0 || cols < 0) return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
   if (rows_valid < 0 || rows_valid > rows)
     return fail(FP8_ERR_SHAPE, "%s: rows_valid=%lld outside [0, %lld]", fn, (long long)rows_valid,
@@ -106,7 +110,8 @@ int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_va
       if (scale || scale_t)
         return fail(FP8_ERR_UNSUPPORTED, "%s: scale/scale_t are outputs of the block modes only", fn);
       return hip_status(
-          fp8lin::launch_quantize_tensorwise(xb, rows, cols, rows_valid, scale_inv, qb, qtb, amax, s),
+          fp8lin::launch_quantize_tensorwise(xb, rows, cols, rows_valid, scale_inv, qb, qtb, amax,
+                                             accumulate, s),
           fn);
     case FP8_BLOCK_1x128:
     case FP8_BLOCK_128x128:
@@ -131,9 +136,13 @@ int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_va
   }
 }
 
-int fp8_scale_update(int mode, const float* amax, float* hist, int32_t len, int32_t pos,
+int fp8_scale_update(int mode, float* amax, float* hist, int32_t len, int32_t pos,
                      float* scale, float* scale_inv, void* stream) {
   const char* fn = "fp8_scale_update";
+  const bool clear = (mode & FP8_SCALE_CLEAR_AMAX) != 0;
+  mode &= ~FP8_SCALE_CLEAR_AMAX;
+  if (clear && mode != FP8_SCALE_FROM_AMAX && mode != FP8_SCALE_RECORD)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: FP8_SCALE_CLEAR_AMAX needs a mode that reads amax", fn);
   switch (mode) {
     case FP8_SCALE_FROM_AMAX:
       if (!amax || !scale || !scale_inv) return fail(FP8_ERR_NULL, "%s: NULL pointer", fn);
@@ -150,8 +159,8 @@ int fp8_scale_update(int mode, const float* amax, float* hist, int32_t len, int3
     default:
       return fail(FP8_ERR_UNSUPPORTED, "%s: unknown mode %d", fn, mode);
   }
-  return hip_status(fp8lin::launch_scale_update(mode, amax, hist, len, pos, scale, scale_inv,
-                                                as_stream(stream)),
+  return hip_status(fp8lin::launch_scale_update(mode, amax, clear, hist, len, pos, scale,
+                                                scale_inv, as_stream(stream)),
                     fn);
 }
 

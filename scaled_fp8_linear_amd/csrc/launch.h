@@ -9,9 +9,10 @@ namespace fp8lin {
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 
+// accumulate: fold max|x| into amax[0] instead of zeroing it first.
 hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t rows, int64_t cols,
                                       int64_t rows_valid, const float* scale_inv, uint8_t* q,
-                                      uint8_t* q_t, float* amax, hipStream_t s);
+                                      uint8_t* q_t, float* amax, bool accumulate, hipStream_t s);
 
 // Block recipe: 1x128 tiles (activations/gradients), 128x128 tiles (weights).
 hipError_t launch_quantize_block_1x128(const uint16_t* x, int64_t rows, int64_t cols,
@@ -21,7 +22,8 @@ hipError_t launch_quantize_block_128x128(const uint16_t* x, int64_t rows, int64_
                                          uint8_t* q, uint8_t* q_t, float* amax, float* scale,
                                          float* scale_t, hipStream_t s);
 
-hipError_t launch_scale_update(int mode, const float* amax, float* hist, int32_t len,
+// clear_amax: set amax[0] to +0 after reading it (modes 0 and 1).
+hipError_t launch_scale_update(int mode, float* amax, bool clear_amax, float* hist, int32_t len,
                                int32_t pos, float* scale, float* scale_inv, hipStream_t s);
 
 hipError_t launch_pad_tokens(const uint16_t* x, int64_t T, int64_t cols, int64_t T_pad,

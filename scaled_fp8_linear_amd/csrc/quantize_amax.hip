@@ -239,16 +239,16 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 
 hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t rows, int64_t cols,
                                       int64_t rows_valid, const float* scale_inv, uint8_t* q,
-                                      uint8_t* q_t, float* amax, hipStream_t s) {
+                                      uint8_t* q_t, float* amax, bool accumulate, hipStream_t s) {
   hipError_t e = hipSuccess;
-  if (amax != nullptr) {
+  if (amax != nullptr && !accumulate) {
     e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 0u, 1, s);
     if (e != hipSuccess) return e;
   }
   if (rows == 0 || cols == 0) return hipSuccess;
   if (q == nullptr && q_t == nullptr && amax == nullptr) return hipSuccess;
   if (rows_valid == 0) {
-    // nothing to read: every code is 0x00 (amax was set to 0 above)
+    // nothing to read: every code is 0x00 (amax was set to 0 above, or keeps its value)
     // (a fill kernel, not a memset: the call may be captured in a graph)
     if (q != nullptr &&
         (e = launch_fill_u32(reinterpret_cast<uint32_t*>(q), 0u, rows * cols / 4, s)) != hipSuccess)

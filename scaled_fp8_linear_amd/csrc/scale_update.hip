@@ -15,16 +15,21 @@ namespace fp8lin {
 
 namespace {
 
-__global__ void scale_from_amax_kernel(const float* __restrict__ amax, float* __restrict__ scale,
-                                       float* __restrict__ scale_inv) {
+// clear: amax[0] = +0 once read (the next quantize pass folds its max into it)
+__global__ void scale_from_amax_kernel(float* __restrict__ amax, float* __restrict__ scale,
+                                       float* __restrict__ scale_inv, int clear) {
+  const float a = amax[0];
   float s, si;
-  scale_pair(amax[0], &s, &si);
+  scale_pair(a, &s, &si);
   scale[0] = s;
   scale_inv[0] = si;
+  if (clear) amax[0] = 0.0f;
 }
 
-__global__ void record_kernel(const float* __restrict__ amax, float* __restrict__ hist, int pos) {
+__global__ void record_kernel(float* __restrict__ amax, float* __restrict__ hist, int pos,
+                              int clear) {
   hist[pos] = amax[0];
+  if (clear) amax[0] = 0.0f;
 }
 
 // One wavefront; len is small (16 for the pages' schedule).
@@ -52,14 +57,16 @@ __global__ void refresh_kernel(const float* __restrict__ hist, int len, float* _
 
 }  // namespace
 
-hipError_t launch_scale_update(int mode, const float* amax, float* hist, int32_t len,
+hipError_t launch_scale_update(int mode, float* amax, bool clear_amax, float* hist, int32_t len,
                                int32_t pos, float* scale, float* scale_inv, hipStream_t s) {
   switch (mode) {
     case 0:
-      hipLaunchKernelGGL(scale_from_amax_kernel, dim3(1), dim3(1), 0, s, amax, scale, scale_inv);
+      hipLaunchKernelGGL(scale_from_amax_kernel, dim3(1), dim3(1), 0, s, amax, scale, scale_inv,
+                         (int)clear_amax);
       break;
     case 1:
-      hipLaunchKernelGGL(record_kernel, dim3(1), dim3(1), 0, s, amax, hist, (int)pos);
+      hipLaunchKernelGGL(record_kernel, dim3(1), dim3(1), 0, s, amax, hist, (int)pos,
+                         (int)clear_amax);
       break;
     case 2:
       hipLaunchKernelGGL(refresh_kernel, dim3(1), dim3(64), 0, s, (const float*)hist, (int)len,

@@ -16,8 +16,10 @@ and step counter, and the order of calls:
 
 Reading: the activation and gradient scales live in two slots (current,
 next) so that wgrad multiplies Qx^T by the scale that produced it, while the
-update for the next step is written as soon as amax is known. Nothing here
-synchronizes with the device.
+update for the next step is written as soon as amax is known. Each amax
+buffer is folded into by its quantize pass (FP8_AMAX_ACCUMULATE) and cleared by
+the update that reads it (FP8_SCALE_CLEAR_AMAX), so no pass needs a separate
+launch to zero it first. Nothing here synchronizes with the device.
 """
 from __future__ import annotations
 
@@ -46,8 +48,12 @@ class DelayedScalingLinear:
     and "scale".
     """
 
-    def __init__(self, device, update_interval: int = 16, probe=None):
+    def __init__(self, device, update_interval: int = 16, probe=None, keep_amax: bool = False):
+        """``keep_amax``: leave each amax in its buffer after the update that reads it (every
+        quantize pass then zeroes its buffer first: one more launch per pass); for
+        inspecting the amaxes of a step."""
         self.probe = probe or _NoProbe()
+        self.acc = not keep_amax
         f32 = dict(dtype=torch.float32, device=device)
         self.update_interval = update_interval
         self.step_count = 0
@@ -61,6 +67,8 @@ class DelayedScalingLinear:
         self.g_scale = torch.ones(2, **f32)
         self.g_scale_inv = torch.ones(2, **f32)
         self.cur = 0
+        # each amax is folded into by one quantize pass and cleared by the update that
+        # reads it, so it is zero whenever a pass starts
         self.amax_w = torch.zeros(1, **f32)
         self.amax_x = torch.zeros(1, **f32)
         self.amax_g = torch.zeros(1, **f32)
@@ -86,23 +94,24 @@ class DelayedScalingLinear:
         with p("quantize"):
             qw, qw_t, _, _, _ = _abi.fp8_quantize_amax(
                 w, scale_inv=self.w_scale_inv, q=b.get("qw"), q_t=b.get("qw_t"), amax=self.amax_w,
-                stream=stream)
+                amax_accumulate=self.acc, stream=stream)
         with p("scale"):
             _abi.fp8_scale_update(_abi.FP8_SCALE_RECORD, amax=self.amax_w, hist=self.hist,
-                                  pos=self.idx, stream=stream)
+                                  pos=self.idx, clear_amax=self.acc, stream=stream)
         self.idx = (self.idx + 1) % self.hist.numel()
         sx, sx_inv = Slot(self.x_scale, self.cur), Slot(self.x_scale_inv, self.cur)
         with p("quantize"):
             qx, qx_t, _, _, _ = _abi.fp8_quantize_amax(
                 x, rows_valid=rows_valid, scale_inv=sx_inv, q=b.get("qx"), q_t=b.get("qx_t"),
-                amax=self.amax_x, stream=stream)
+                amax=self.amax_x, amax_accumulate=self.acc, stream=stream)
         with p("gemm"):
             y = _abi.fp8_linear_fwd(qx, qw, sx, self.w_scale, y=out, M_valid=rows_valid,
                                     stream=stream)
         with p("scale"):
             _abi.fp8_scale_update(_abi.FP8_SCALE_FROM_AMAX, amax=self.amax_x,
                                   scale=Slot(self.x_scale, self.nxt),
-                                  scale_inv=Slot(self.x_scale_inv, self.nxt), stream=stream)
+                                  scale_inv=Slot(self.x_scale_inv, self.nxt), clear_amax=self.acc,
+                                  stream=stream)
         self._saved = (qx_t, qw_t, rows_valid)
         return y
 
@@ -115,7 +124,7 @@ class DelayedScalingLinear:
         with p("quantize"):
             qg, qg_t, _, _, _ = _abi.fp8_quantize_amax(
                 g, rows_valid=rows_valid, scale_inv=sg_inv, q=b.get("qg"), q_t=b.get("qg_t"),
-                amax=self.amax_g, stream=stream)
+                amax=self.amax_g, amax_accumulate=self.acc, stream=stream)
         with p("gemm"):
             dx = _abi.fp8_linear_dgrad(qg, qw_t, sg, self.w_scale, dx=dx, M_valid=rows_valid,
                                        stream=stream)
@@ -125,7 +134,8 @@ class DelayedScalingLinear:
         with p("scale"):
             _abi.fp8_scale_update(_abi.FP8_SCALE_FROM_AMAX, amax=self.amax_g,
                                   scale=Slot(self.g_scale, self.nxt),
-                                  scale_inv=Slot(self.g_scale_inv, self.nxt), stream=stream)
+                                  scale_inv=Slot(self.g_scale_inv, self.nxt), clear_amax=self.acc,
+                                  stream=stream)
         return dx, dw
 
     def end_step(self) -> None:

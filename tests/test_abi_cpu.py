@@ -94,3 +94,13 @@ def test_pad_tokens_query(lib):
         assert out.value == want
     assert lib.fp8_pad_tokens(None, 5, 8, 0, None, ctypes.byref(out), None) == 2
     assert lib.fp8_pad_tokens(None, 5, 8, 16, None, None, None) == 1
+
+
+def test_amax_flag_checks(lib):
+    p = ctypes.c_void_p(16)
+    # accumulate is for tensorwise passes only
+    assert lib.fp8_quantize_amax(p, 128, 128, 128, 1 | 0x100, None, p, None, p, p, None,
+                                 None) == 4
+    # clear needs a mode that reads amax
+    assert lib.fp8_scale_update(2 | 0x100, p, p, 16, 0, p, p, None) == 4
+    assert lib.fp8_scale_update(0 | 0x100, None, None, 0, 0, p, p, None) == 1

@@ -39,8 +39,12 @@ def _scales_equal(gpu: dict, ref: dict, what: str) -> None:
 
 
 def test_small_shape_every_byte_20_steps(lib):
+    """Every code, amax and scale of 20 delayed-scaling steps against the oracle. The layer
+    under test keeps its amaxes for inspection; a second layer in the default mode (amax
+    folded into a buffer that the scale update clears) must produce the same bytes."""
     M, K, N, rv = 272, 384, 400, 250
-    lin = lib.DelayedScalingLinear("cuda")
+    lin = lib.DelayedScalingLinear("cuda", keep_amax=True)
+    lin2 = lib.DelayedScalingLinear("cuda")
     ref = DelayedLinear()
     w = workloads.linear_inputs(2, 0, M=M, K=K, N=N)["w"]
     for t in range(1, 21):
@@ -54,7 +58,17 @@ def test_small_shape_every_byte_20_steps(lib):
         y = lin.forward(dev_bf16(x), dev_bf16(w), rows_valid=rv, bufs=bufs)
         dx, dw = lin.backward(dev_bf16(g))
         qx_t, qw_t, _ = lin._saved
+        lin2.begin_step()
+        y2 = lin2.forward(dev_bf16(x), dev_bf16(w), rows_valid=rv)
+        dx2, dw2 = lin2.backward(dev_bf16(g))
+        qx_t2, qw_t2, _ = lin2._saved
         torch.cuda.synchronize()
+        assert torch.equal(qx_t, qx_t2) and torch.equal(qw_t, qw_t2), f"codes step {t}"
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"y step {t}"
+        assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16)), f"dx step {t}"
+        assert torch.equal(dw.view(torch.int16), dw2.view(torch.int16)), f"dw step {t}"
+        assert f32_bits(lin2.amax_x.item()) == f32_bits(lin2.amax_g.item()) == 0
+        assert f32_bits(lin2.amax_w.item()) == 0
         ref.begin_step()
         f = ref.forward(x, w, rows_valid=rv)
         b = ref.backward(g)
@@ -70,7 +84,9 @@ def test_small_shape_every_byte_20_steps(lib):
         assert_within(host_bf16_f64(dw), b["dw"],
                       gemm.error_bound(b["qg_t"], f["qx_t"], b["sg"], f["sx"]), f"dw step {t}")
         lin.end_step()
+        lin2.end_step()
         _scales_equal(lin.state(), ref.state(), f"step {t}")
+        _scales_equal(lin2.state(), ref.state(), f"default mode, step {t}")
         w = workloads.drift(w, 2, t, 1e-4)
 
 
@@ -79,7 +95,7 @@ def test_config2_full_size_32_step_trajectory(lib):
     g ~ N(0,1e-3); 32 steps of delayed scaling."""
     c = workloads.CONFIGS[2]
     M, K, N = c["M"], c["K"], c["N"]
-    lin = lib.DelayedScalingLinear("cuda")
+    lin = lib.DelayedScalingLinear("cuda", keep_amax=True)
     ref = DelayedLinear()
     w = workloads.linear_inputs(2, 0)["w"]
     rng = np.random.default_rng(2)
@@ -149,7 +165,7 @@ def test_config4_packed_varlen(lib, count, len_hi):
     assert torch.all(xp[T:] == 0).item() and torch.all(gbuf[T:] == 0).item()
     assert torch.equal(xp[:T].view(torch.int16), xd.view(torch.int16))
     # rows_valid = T on top: the sentinel-free padded rows must still be excluded
-    lin = lib.DelayedScalingLinear("cuda")
+    lin = lib.DelayedScalingLinear("cuda", keep_amax=True)
     lin.begin_step()
     y = lin.forward(xp, dev_bf16(w), rows_valid=T)
     dx, dw = lin.backward(gbuf)

@@ -107,6 +107,48 @@ def test_amax_only_and_q_only(lib):
     assert_same_bytes(host_u8(q), quantize_values(x, np.float32(7.0)), "q only")
 
 
+def test_amax_accumulate_and_clear(lib):
+    """FP8_AMAX_ACCUMULATE folds max|x| into the amax buffer's value; FP8_SCALE_CLEAR_AMAX
+    leaves +0 in it after the update that reads it (FROM_AMAX and RECORD)."""
+    x = workloads.bf16_tensor("student_t", (272, 528), 93, 2, 0, nu=3)
+    oa = o_amax(x)
+    si = np.float32(448.0) / oa
+    for prior in (np.float32(0.0), np.float32(oa * 4), np.float32(oa / 4)):
+        note(f"quantize with amax accumulate, prior {prior}")
+        a = dev_f32(prior)
+        q, qt, a2, _, _ = lib.fp8_quantize_amax(dev_bf16(x), scale_inv=dev_f32(si), amax=a,
+                                                amax_accumulate=True)
+        torch.cuda.synchronize()
+        assert a2 is a
+        assert f32_bits(a.item()) == f32_bits(max(prior, oa)), (prior, a.item(), oa)
+        oq, oqt, _ = quantize_tensorwise(x, si)
+        assert_same_bytes(host_u8(q), oq, "q with accumulate")
+        assert_same_bytes(host_u8(qt), oqt, "q_t with accumulate")
+    note("quantize with amax accumulate, no valid rows")
+    a = dev_f32(3.0)
+    lib.fp8_quantize_amax(dev_bf16(x), rows_valid=0, scale_inv=dev_f32(si), amax=a,
+                          amax_accumulate=True)
+    torch.cuda.synchronize()
+    assert a.item() == 3.0
+    note("scale update FROM_AMAX with clear")
+    a = dev_f32(oa)
+    s_ = torch.empty(1, device="cuda")
+    si_ = torch.empty(1, device="cuda")
+    lib.fp8_scale_update(lib.FP8_SCALE_FROM_AMAX, amax=a, scale=s_, scale_inv=si_, clear_amax=True)
+    torch.cuda.synchronize()
+    os_, osi = scale_from_amax(oa)
+    assert f32_bits(s_.item()) == f32_bits(os_) and f32_bits(si_.item()) == f32_bits(osi)
+    assert f32_bits(a.item()) == 0
+    note("scale update RECORD with clear")
+    a = dev_f32(oa)
+    hist = torch.ones(16, device="cuda")
+    lib.fp8_scale_update(lib.FP8_SCALE_RECORD, amax=a, hist=hist, pos=5, clear_amax=True)
+    torch.cuda.synchronize()
+    h = hist.cpu().numpy()
+    assert f32_bits(h[5]) == f32_bits(oa) and np.all(np.delete(h, 5) == 1.0)
+    assert f32_bits(a.item()) == 0
+
+
 def test_current_scaling_config1(lib):
     """Config 1's forward quantize: amax pass, scale, then the cast (all on the device)."""
     d = workloads.linear_inputs(1)
