@@ -78,9 +78,13 @@ class DelayedScalingLinear:
     def nxt(self) -> int:
         return 1 - self.cur
 
-    def begin_step(self, stream=None) -> bool:
+    def begin_step(self, stream=None, refresh: bool | None = None) -> bool:
+        """Advance one step; refresh the weight scale from the ring every update_interval
+        steps (or as ``refresh`` says, when a caller keeps the step count globally)."""
         self.step_count += 1
-        if self.step_count % self.update_interval == 0:
+        if refresh is None:
+            refresh = self.step_count % self.update_interval == 0
+        if refresh:
             with self.probe("scale"):
                 _abi.fp8_scale_update(_abi.FP8_SCALE_REFRESH, hist=self.hist, scale=self.w_scale,
                                       scale_inv=self.w_scale_inv, stream=stream)
@@ -138,8 +142,30 @@ class DelayedScalingLinear:
                                   stream=stream)
         return dx, dw
 
-    def end_step(self) -> None:
+    def end_step(self, g_updated: bool = True) -> None:
+        """The next slots become current. ``g_updated`` False (a step without backward):
+        the gradient scale carries over unchanged."""
+        if not g_updated:
+            self.g_scale[self.nxt:self.nxt + 1].copy_(self.g_scale[self.cur:self.cur + 1])
+            self.g_scale_inv[self.nxt:self.nxt + 1].copy_(self.g_scale_inv[self.cur:self.cur + 1])
         self.cur = self.nxt
+
+    _TENSORS = ("w_scale", "w_scale_inv", "hist", "x_scale", "x_scale_inv", "g_scale",
+                "g_scale_inv")
+
+    def state_dict(self) -> dict:
+        """The whole schedule state: device tensors cloned, host counters as ints."""
+        d = {k: getattr(self, k).detach().clone() for k in self._TENSORS}
+        d.update(step_count=self.step_count, idx=self.idx, cur=self.cur,
+                 update_interval=self.update_interval)
+        return d
+
+    def load_state_dict(self, d: dict) -> None:
+        if int(d["update_interval"]) != self.update_interval:
+            raise ValueError("update_interval differs from the saved state's")
+        for k in self._TENSORS:
+            getattr(self, k).copy_(d[k])
+        self.step_count, self.idx, self.cur = int(d["step_count"]), int(d["idx"]), int(d["cur"])
 
     def state(self) -> dict:
         """Host copies of the schedule state (synchronizes; for tests)."""
