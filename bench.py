@@ -334,21 +334,96 @@ def measure_varlen(torch, m, workloads, steps, warmup):
     _, T_pad = m.fp8_pad_tokens(x, query_only=True)
     xp = torch.empty((T_pad, x.shape[1]), dtype=x.dtype, device=dev)
     gp = torch.empty((T_pad, g.shape[1]), dtype=g.dtype, device=dev)
+    # the packed batches as a loader would hand them over: in buffers with room for T_pad
+    # rows, the tail holding whatever was there before
+    xb = torch.full((T_pad, x.shape[1]), float("nan"), dtype=x.dtype, device=dev)
+    gb = torch.full((T_pad, g.shape[1]), float("nan"), dtype=g.dtype, device=dev)
+    xb[:T].copy_(x)
+    gb[:T].copy_(g)
     lin = m.DelayedScalingLinear(dev)
 
-    def step():
-        m.fp8_pad_tokens(x, x_pad=xp)
+    def step_in_place():
+        m.fp8_pad_tokens(xb, T=T, x_pad=xb)         # zero rows [T, T_pad) of the batch
+        m.fp8_pad_tokens(gb, T=T, x_pad=gb)
+        lin.begin_step()
+        lin.forward(xb, w, rows_valid=T)
+        lin.backward(gb)
+        lin.end_step()
+
+    def step_copy():
+        m.fp8_pad_tokens(x, x_pad=xp)               # copy [T] rows into a [T_pad] buffer
         m.fp8_pad_tokens(g, x_pad=gp)
         lin.begin_step()
         lin.forward(xp, w, rows_valid=T)
         lin.backward(gp)
         lin.end_step()
 
-    ms = _time_steps(torch, step, steps, warmup)
+    ms = _time_steps(torch, step_in_place, steps, warmup)
+    ms_copy = _time_steps(torch, step_copy, steps, warmup)
     flops = 6.0 * T_pad * 4096 * 4096
     return {"workload": "packed THD batch, 64 seqs U{32..2048}, K=N=4096, delayed scaling",
             "tokens": T, "tokens_padded": T_pad, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-            "ms_per_step": round(ms, 4)}
+            "ms_per_step": round(ms, 4), "padding": "in place (tail rows of the batch zeroed)",
+            "ms_per_step_padding_by_copy": round(ms_copy, 4)}
+
+
+def measure_f1(torch, m, steps, warmup):
+    """The autograd wrapper with bias at the gate linear's shape (tokens 8192, 4096 -> 14336):
+    the forward GEMM with and without the bias epilogue (HIP events per launch), the bias
+    gradient pass (GB/s), and whole Fp8Linear fwd+bwd steps through torch.autograd."""
+    M, K, N = 8192, 4096, 14336
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(1)
+    x = torch.randn(M, K, device=dev, generator=gen).to(torch.bfloat16)
+    g = (torch.randn(M, N, device=dev, generator=gen) * 1e-3).to(torch.bfloat16)
+    layer = m.Fp8Linear(K, N, bias=True, device=dev)
+    qx = m.fp8_quantize_amax(x, scale_inv=torch.ones(1, device=dev), want_q_t=False)[0]
+    qw = m.fp8_quantize_amax(layer.weight.detach(), scale_inv=torch.full((1,), 64.0, device=dev),
+                             want_q_t=False)[0]
+    one = torch.ones(1, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    b = layer.bias.detach()
+
+    def per_launch_us(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, c in ev:
+            a.record()
+            fn()
+            c.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(c) for a, c in ev])) * 1e3
+
+    us_plain = per_launch_us(lambda: m.fp8_linear_fwd(qx, qw, one, one, y=y), steps)
+    us_bias = per_launch_us(lambda: m.fp8_linear_fwd(qx, qw, one, one, y=y, bias=b), steps)
+    db = torch.empty(N, dtype=torch.bfloat16, device=dev)
+    us_db = per_launch_us(lambda: m.fp8_bias_grad(g, db=db), steps)
+
+    m.fp8_state().reset()
+    xr = x.detach().requires_grad_(True)
+
+    def step():
+        layer.weight.grad = None
+        layer.bias.grad = None
+        xr.grad = None
+        with m.fp8_autocast():
+            out = layer(xr)
+        out.backward(g)
+
+    ms = _time_steps(torch, step, steps, warmup)
+    m.fp8_state().reset()
+    flops = 6.0 * M * N * K
+    return {"workload": "Fp8Linear(4096 -> 14336, bias) fwd+bwd through torch.autograd, tokens 8192",
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "ms_per_step": round(ms, 4),
+            "fwd_gemm_us": round(us_plain, 1), "fwd_gemm_with_bias_us": round(us_bias, 1),
+            "bias_epilogue_overhead": round(us_bias / us_plain - 1.0, 4),
+            "bias_grad_us": round(us_db, 1),
+            "bias_grad_gbs": round(2.0 * M * N / (us_db * 1e-6) / 1e9, 1),
+            "bias_grad_frac_of_hbm_peak": round(2.0 * M * N / (us_db * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                                4)}
 
 
 def main():
@@ -497,6 +572,7 @@ def main():
         line["other_rows"] = {
             "block_recipe": measure_block_recipe(torch, m, workloads, max(3, args.steps // 3), 2),
             "packed_varlen_padding": measure_varlen(torch, m, workloads, max(3, args.steps // 3), 2),
+            "autograd_bias_f1": measure_f1(torch, m, max(3, args.steps // 3), 2),
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)

@@ -219,6 +219,39 @@ int fp8_linear_wgrad(const void* qg_t, const void* qx_t, const float* sg, const 
                      int64_t M, int64_t N, int64_t K, int gran, void* stream);
 
 /*
+ * fp8_linear_fwd_bias -- fp8_linear_fwd with a bias added in the GEMM's epilogue.
+ *
+ * Source: [AstrAI] fp8_linear_forward(x, w, bias): the bias goes to the scaled
+ * forward kernel with the operands.
+ *
+ *   bias  bf16 [N] or NULL (NULL: exactly fp8_linear_fwd). FP8_TENSORWISE only.
+ *   y     y[m,n] = bf16_rne(float32(sx * sw * sum_k qx[m,k] * qw[n,k]) + float32(bias[n]))
+ *         for m < M_valid (one rounding, after the bias), 0 otherwise; with K = 0
+ *         the valid rows are the bias.
+ *   Other arguments and errors as fp8_linear_fwd; bias must be 16-byte aligned.
+ */
+int fp8_linear_fwd_bias(const void* qx, const void* qw, const float* sx, const float* sw,
+                        const void* bias, void* y, int64_t M, int64_t N, int64_t K,
+                        int64_t M_valid, int gran, void* stream);
+
+/*
+ * fp8_bias_grad -- the bias gradient: column sums of the output gradient.
+ *
+ * Source: [AstrAI] fp8_linear_backward(g, x, w, masks): masks select the input,
+ * weight and bias gradients of the linear.
+ *
+ *   g     bf16 [rows, cols], cols a multiple of 16; rows r >= rows_valid are token
+ *         padding and are not read.
+ *   db    bf16 [cols]: db[c] = bf16_rne(sum over r < rows_valid of float32(g[r,c])),
+ *         float32 sums in a fixed order (the same result on every call); 0 if
+ *         rows_valid = 0.
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN (g 16-byte aligned),
+ * FP8_ERR_UNSUPPORTED (g of 2^31 bytes or more), FP8_ERR_HIP.
+ */
+int fp8_bias_grad(const void* g, int64_t rows, int64_t cols, int64_t rows_valid, void* db,
+                  void* stream);
+
+/*
  * fp8_pad_tokens -- pad a packed token batch to a multiple of `multiple` rows.
  *
  * Source: [NeMo] review thread, "pad = (-T) % seq_multiple"; [SpecForge]

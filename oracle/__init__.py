@@ -28,6 +28,8 @@ Modules:
 * ``scaling``   -- scale from amax, the weight amax-history ring, and the
                    per-step delayed-scaling schedule of one linear layer.
 * ``gemm``      -- the exact scaled GEMM in float64 and its error bound.
+* ``bias``      -- the bias added to the forward output, and the bias gradient
+                   (column sums of the output gradient), with their tolerances.
 * ``padding``   -- token-count padding to a multiple.
 * ``block``     -- the block-scaled recipe (1x128 / 128x128 tiles).
 

@@ -8,13 +8,14 @@ library; calling any entry point without it raises.
 """
 from ._abi import (FP8_AMAX_ACCUMULATE, FP8_BLOCK_1x128, FP8_BLOCK_128x128, FP8_SCALE_CLEAR_AMAX,
                    FP8_SCALE_FROM_AMAX, FP8_SCALE_RECORD, FP8_SCALE_REFRESH, FP8_TENSORWISE,
-                   Fp8Error, Slot, fp8_last_error,
+                   Fp8Error, Slot, fp8_bias_grad, fp8_last_error,
                    fp8_linear_dgrad, fp8_linear_fwd, fp8_linear_wgrad, fp8_pad_tokens,
                    fp8_quantize_amax, fp8_scale_update, fp8_version, load)
 from .autograd import Fp8Linear, fp8_autocast, fp8_state
 from .state import DelayedScalingLinear
 
 __all__ = ["fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
+           "fp8_bias_grad",
            "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version", "load",
            "Fp8Error", "Slot", "DelayedScalingLinear", "FP8_TENSORWISE", "FP8_BLOCK_1x128",
            "FP8_BLOCK_128x128", "FP8_SCALE_FROM_AMAX", "FP8_SCALE_RECORD", "FP8_SCALE_REFRESH",

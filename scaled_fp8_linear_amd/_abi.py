@@ -23,7 +23,8 @@ FP8_AMAX_ACCUMULATE = 0x100     # flag for fp8_quantize_amax (tensorwise)
 FP8_SCALE_CLEAR_AMAX = 0x100    # flag for fp8_scale_update (FROM_AMAX, RECORD)
 
 EXPORTS = ("fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
-           "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version")
+           "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version",
+           "fp8_linear_fwd_bias", "fp8_bias_grad")
 
 
 class Fp8Error(RuntimeError):
@@ -51,6 +52,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_quantize_amax.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.fp8_scale_update.argtypes = [_int, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
     lib.fp8_linear_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
+    lib.fp8_linear_fwd_bias.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                        _int, _vp]
+    lib.fp8_bias_grad.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
     lib.fp8_linear_dgrad.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
     lib.fp8_linear_wgrad.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]
     lib.fp8_pad_tokens.argtypes = [_vp, _i64, _i64, _i32, _vp, ctypes.POINTER(_i64), _vp]
@@ -179,8 +183,9 @@ def fp8_scale_update(mode, amax=None, hist=None, pos=0, scale=None, scale_inv=No
         _fptr(scale, "scale"), _fptr(scale_inv, "scale_inv"), _stream(stream)))
 
 
-def fp8_linear_fwd(qx, qw, sx, sw, y=None, M_valid=None, gran=FP8_TENSORWISE, stream=None):
-    """y [M, N] bf16 = sx * sw * qx [M, K] . qw [N, K]^T."""
+def fp8_linear_fwd(qx, qw, sx, sw, y=None, M_valid=None, gran=FP8_TENSORWISE, stream=None,
+                   bias=None):
+    """y [M, N] bf16 = sx * sw * qx [M, K] . qw [N, K]^T (+ bias [N], bf16, in the epilogue)."""
     qx, qw = _codes(qx), _codes(qw)
     M, K = qx.shape
     N = qw.shape[0]
@@ -189,10 +194,30 @@ def fp8_linear_fwd(qx, qw, sx, sw, y=None, M_valid=None, gran=FP8_TENSORWISE, st
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
     mv = M if M_valid is None else int(M_valid)
+    if bias is not None:
+        _bf16(bias)
+        if tuple(bias.shape) != (N,):
+            raise ValueError(f"bias must be [{N}]")
+        _check("fp8_linear_fwd_bias", load().fp8_linear_fwd_bias(
+            _ptr(qx), _ptr(qw), _fptr(sx, "sx"), _fptr(sw, "sw"), _ptr(bias), _ptr(y), M, N, K,
+            mv, gran, _stream(stream)))
+        return y
     _check("fp8_linear_fwd", load().fp8_linear_fwd(
         _ptr(qx), _ptr(qw), _fptr(sx, "sx"), _fptr(sw, "sw"), _ptr(y), M, N, K, mv, gran,
         _stream(stream)))
     return y
+
+
+def fp8_bias_grad(g, rows_valid=None, db=None, stream=None):
+    """db [cols] bf16 = column sums of g [rows, cols] over the valid rows (float32 sums)."""
+    _bf16(g)
+    rows, cols = g.shape
+    rv = rows if rows_valid is None else int(rows_valid)
+    if db is None:
+        db = torch.empty(cols, dtype=torch.bfloat16, device=g.device)
+    _check("fp8_bias_grad", load().fp8_bias_grad(_ptr(g), rows, cols, rv, _ptr(db),
+                                                 _stream(stream)))
+    return db
 
 
 def fp8_linear_dgrad(qg, qw_t, sg, sw, dx=None, M_valid=None, gran=FP8_TENSORWISE, stream=None):

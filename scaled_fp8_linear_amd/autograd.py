@@ -80,11 +80,12 @@ class _Fp8LinearFn(torch.autograd.Function):
     with the padded rows kept out of amax and outputs (rows_valid), and cut off again."""
 
     @staticmethod
-    def forward(ctx, x2d, weight, layer):
+    def forward(ctx, x2d, weight, bias, layer):
         M = x2d.shape[0]
         xp, M_pad = _abi.fp8_pad_tokens(x2d) if M % 16 else (x2d, M)
-        y = layer._lin.forward(xp, weight.detach(), rows_valid=M)
-        ctx.layer, ctx.M, ctx.M_pad = layer, M, M_pad
+        b = None if bias is None else bias.detach()
+        y = layer._lin.forward(xp, weight.detach(), rows_valid=M, bias=b)
+        ctx.layer, ctx.M, ctx.M_pad, ctx.has_bias = layer, M, M_pad, bias is not None
         return y[:M] if M_pad != M else y
 
     @staticmethod
@@ -96,14 +97,17 @@ class _Fp8LinearFn(torch.autograd.Function):
         if ctx.M_pad != ctx.M:
             gy, _ = _abi.fp8_pad_tokens(gy)
         dx, dw = layer._lin.backward(gy)
+        db = _abi.fp8_bias_grad(gy, rows_valid=ctx.M) if ctx.has_bias else None
         layer._lin.end_step()
         layer._pending = False
-        return (dx[:ctx.M] if ctx.M_pad != ctx.M else dx), dw, None
+        return (dx[:ctx.M] if ctx.M_pad != ctx.M else dx), dw, db, None
 
 
 class Fp8Linear(torch.nn.Module):
-    """A bias-free linear layer y = x W^T with a bf16 weight [out, in] that runs as the
-    scaled FP8 linear inside ``fp8_autocast`` (delayed scaling, e4m3 operands, bf16 out).
+    """A linear layer y = x W^T (+ b) with a bf16 weight [out, in] (and bias [out]) that
+    runs as the scaled FP8 linear inside ``fp8_autocast`` (delayed scaling, e4m3 operands,
+    the bias added in the GEMM's epilogue, bf16 out; the bias gradient is a column sum of
+    the output gradient).
 
     in_features and out_features must be multiples of 16 for the fp8 path (the fp8 GEMMs
     need it); the token count need not be: the layer pads it with fp8_pad_tokens and keeps
@@ -111,7 +115,7 @@ class Fp8Linear(torch.nn.Module):
     scales, slots, counters) is saved and restored with the module's state_dict.
     """
 
-    def __init__(self, in_features: int, out_features: int, device=None,
+    def __init__(self, in_features: int, out_features: int, bias: bool = False, device=None,
                  update_interval: int = 16):
         super().__init__()
         self.in_features, self.out_features = in_features, out_features
@@ -119,6 +123,12 @@ class Fp8Linear(torch.nn.Module):
             torch.empty((out_features, in_features), dtype=torch.bfloat16, device=device))
         bound = 1.0 / math.sqrt(in_features)          # nn.Linear's default initialisation
         torch.nn.init.uniform_(self.weight, -bound, bound)
+        if bias:
+            self.bias = torch.nn.Parameter(
+                torch.empty(out_features, dtype=torch.bfloat16, device=device))
+            torch.nn.init.uniform_(self.bias, -bound, bound)
+        else:
+            self.register_parameter("bias", None)
         self.update_interval = update_interval
         self._lin = None
         self._generation = -1
@@ -145,7 +155,7 @@ class Fp8Linear(torch.nn.Module):
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if not _state.enabled or not self._fp8_ok():
-            return F.linear(x, self.weight)
+            return F.linear(x, self.weight, self.bias)
         if x.shape[-1] != self.in_features:
             raise ValueError(f"expected {self.in_features} input features, got {x.shape[-1]}")
         self._begin()
@@ -156,11 +166,13 @@ class Fp8Linear(torch.nn.Module):
         x2d = x2d.contiguous()
         # the step ends after the backward, or (none run) when the layer's next step begins
         self._pending = True
-        if torch.is_grad_enabled() and (x.requires_grad or self.weight.requires_grad):
-            y = _Fp8LinearFn.apply(x2d, self.weight, self)
+        b = self.bias
+        if torch.is_grad_enabled() and (x.requires_grad or self.weight.requires_grad or
+                                        (b is not None and b.requires_grad)):
+            y = _Fp8LinearFn.apply(x2d, self.weight, b, self)
         else:
             with torch.no_grad():
-                y = _Fp8LinearFn.forward(_NoCtx(), x2d, self.weight, self)
+                y = _Fp8LinearFn.forward(_NoCtx(), x2d, self.weight, b, self)
         return y.reshape(*lead, self.out_features)
 
     # delayed-scaling state in the module's state_dict

@@ -171,10 +171,49 @@ int fp8_linear_fwd(const void* qx, const void* qw, const float* sx, const float*
   if (gran == FP8_BLOCK_1x128 && N % 128)
     return fail(FP8_ERR_SHAPE, "fp8_linear_fwd: block recipe needs N %% 128 == 0");
   return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qx),
-                                            static_cast<const uint8_t*>(qw), sx, sw,
+                                            static_cast<const uint8_t*>(qw), sx, sw, nullptr,
                                             static_cast<uint16_t*>(y), M, N, K, M_valid,
                                             gran == FP8_BLOCK_1x128, 128, as_stream(stream)),
                     "fp8_linear_fwd");
+}
+
+int fp8_linear_fwd_bias(const void* qx, const void* qw, const float* sx, const float* sw,
+                        const void* bias, void* y, int64_t M, int64_t N, int64_t K,
+                        int64_t M_valid, int gran, void* stream) {
+  const char* fn = "fp8_linear_fwd_bias";
+  if (bias == nullptr)
+    return fp8_linear_fwd(qx, qw, sx, sw, y, M, N, K, M_valid, gran, stream);
+  int e = check_gemm(fn, qx, qw, sx, sw, y, M, N, K, M_valid, gran);
+  if (e) return e;
+  if (gran != FP8_TENSORWISE)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: the bias epilogue is for FP8_TENSORWISE", fn);
+  if (!aligned16(bias)) return fail(FP8_ERR_ALIGN, "%s: bias must be 16-byte aligned", fn);
+  return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qx),
+                                            static_cast<const uint8_t*>(qw), sx, sw,
+                                            static_cast<const uint16_t*>(bias),
+                                            static_cast<uint16_t*>(y), M, N, K, M_valid, false,
+                                            128, as_stream(stream)),
+                    fn);
+}
+
+int fp8_bias_grad(const void* g, int64_t rows, int64_t cols, int64_t rows_valid, void* db,
+                  void* stream) {
+  const char* fn = "fp8_bias_grad";
+  if (rows < 0 || cols < 0) return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
+  if (cols % 16) return fail(FP8_ERR_SHAPE, "%s: cols=%lld not a multiple of 16", fn,
+                             (long long)cols);
+  if (rows_valid < 0 || rows_valid > rows)
+    return fail(FP8_ERR_SHAPE, "%s: rows_valid=%lld outside [0, %lld]", fn,
+                (long long)rows_valid, (long long)rows);
+  if (cols > 0 && !db) return fail(FP8_ERR_NULL, "%s: db is NULL", fn);
+  if (rows_valid > 0 && cols > 0 && !g) return fail(FP8_ERR_NULL, "%s: g is NULL", fn);
+  if (!aligned16(g)) return fail(FP8_ERR_ALIGN, "%s: g must be 16-byte aligned", fn);
+  if (rows * cols * 2 >= kMaxOperandBytes)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: g holds 2^31 bytes or more", fn);
+  return hip_status(fp8lin::launch_bias_grad(static_cast<const uint16_t*>(g), rows, cols,
+                                             rows_valid, static_cast<uint16_t*>(db),
+                                             as_stream(stream)),
+                    fn);
 }
 
 int fp8_linear_dgrad(const void* qg, const void* qw_t, const float* sg, const float* sw, void* dx,
@@ -184,7 +223,7 @@ int fp8_linear_dgrad(const void* qg, const void* qw_t, const float* sg, const fl
   if (gran == FP8_BLOCK_1x128 && K % 128)
     return fail(FP8_ERR_SHAPE, "fp8_linear_dgrad: block recipe needs K %% 128 == 0");
   return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qg),
-                                            static_cast<const uint8_t*>(qw_t), sg, sw,
+                                            static_cast<const uint8_t*>(qw_t), sg, sw, nullptr,
                                             static_cast<uint16_t*>(dx), M, K, N, M_valid,
                                             gran == FP8_BLOCK_1x128, 128, as_stream(stream)),
                     "fp8_linear_dgrad");
@@ -195,7 +234,7 @@ int fp8_linear_wgrad(const void* qg_t, const void* qx_t, const float* sg, const 
   int e = check_gemm("fp8_linear_wgrad", qg_t, qx_t, sg, sx, dw, N, K, M, N, gran);
   if (e) return e;
   return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qg_t),
-                                            static_cast<const uint8_t*>(qx_t), sg, sx,
+                                            static_cast<const uint8_t*>(qx_t), sg, sx, nullptr,
                                             static_cast<uint16_t*>(dw), N, K, M, N,
                                             gran == FP8_BLOCK_1x128, 1, as_stream(stream)),
                     "fp8_linear_wgrad");

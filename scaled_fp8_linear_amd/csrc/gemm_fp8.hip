@@ -91,6 +91,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // right for groups of 16 consecutive lanes, costs a second cycle per read here).
 __device__ __forceinline__ int row_swizzle(int r) { return (r >> 1) & 5; }
 
+// bias epilogue: 4 consecutive bf16 bias values (8 bytes at column n, n a multiple of 4)
+// as floats; columns past N read as 0 (their outputs are dropped anyway)
+__device__ __forceinline__ v4f bias4(const uint16_t* bias, int n, int N) {
+  if (n >= N) return v4f{0.f, 0.f, 0.f, 0.f};
+  const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
+  return v4f{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+             __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u)};
+}
+
 // 16-byte LDS read at an LDS byte address (a base register plus a constant folds into the
 // instruction's offset field)
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -193,6 +202,7 @@ struct Tile {
   int wave, wm, wn, fr, fg, ch, r0, c_lo, c_hi;
   uint32_t step_rows;
   float s_tensor;   // tensorwise: sa * sb (wave-uniform)
+  const uint16_t* bias = nullptr;   // tensorwise: bf16 [N] added after scaling, or none
 
   v16f acc[C::TM][C::TN];
   v16f part[C::BLOCK ? C::TM : 1][C::BLOCK ? C::TN : 1];
@@ -340,6 +350,8 @@ struct Tile {
   // write the tile at (m0, n0): scale, round to bf16, 16 bytes per lane. Every lane
   // issues exactly 2 TM TN buffer stores; pieces outside D get an offset past its end,
   // which the buffer range check drops.
+  // With a bias, value 4 rq + c of the lane holds column 32 j + 8 rq + 4 fg + c of its
+  // 32x32 tile; the bias is added in float32 after the scale, before the one rounding.
   __device__ void epilogue(int m0, int n0) {
     const float s = s_tensor;
 #pragma unroll
@@ -355,8 +367,16 @@ struct Tile {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int rq = 2 * p + h;
-            q[h][0] = pack_bf16x2(acc[i][j][4 * rq + 0] * s, acc[i][j][4 * rq + 1] * s);
-            q[h][1] = pack_bf16x2(acc[i][j][4 * rq + 2] * s, acc[i][j][4 * rq + 3] * s);
+            if (bias != nullptr) {
+              const v4f b = bias4(bias, n0 + wn * C::WTN + 32 * j + 8 * rq + 4 * fg, N);
+              q[h][0] = pack_bf16x2(acc[i][j][4 * rq + 0] * s + b[0],
+                                    acc[i][j][4 * rq + 1] * s + b[1]);
+              q[h][1] = pack_bf16x2(acc[i][j][4 * rq + 2] * s + b[2],
+                                    acc[i][j][4 * rq + 3] * s + b[3]);
+            } else {
+              q[h][0] = pack_bf16x2(acc[i][j][4 * rq + 0] * s, acc[i][j][4 * rq + 1] * s);
+              q[h][1] = pack_bf16x2(acc[i][j][4 * rq + 2] * s, acc[i][j][4 * rq + 3] * s);
+            }
           }
           const auto w0 = __builtin_amdgcn_permlane32_swap(q[0][0], q[1][0], false, false);
           const auto w1 = __builtin_amdgcn_permlane32_swap(q[0][1], q[1][1], false, false);
@@ -380,8 +400,9 @@ template <class C>
 __global__ void __launch_bounds__(C::kThreads, 1)
 gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                         const float* __restrict__ sa, const float* __restrict__ sb,
-                        uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
-                        int tiles_n, int split_m, int split_n) {
+                        const uint16_t* __restrict__ bias, uint16_t* __restrict__ D, int M,
+                        int N, int K, int M_valid, int tiles_m, int tiles_n, int split_m,
+                        int split_n) {
   constexpr int SB = C::kStageBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t s0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[SB];
@@ -391,6 +412,7 @@ gemm_fp8_persist_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict
 
   Tile<C> T;
   T.init(A, B, sa, sb, D, M, N, K, M_valid);
+  T.bias = bias;
 
   // ---- this workgroup's tiles. With split_m * split_n = 8 the tile grid is cut into
   // 8 rectangles, one per XCD (workgroup b runs on XCD b % 8); the workgroups of an
@@ -496,12 +518,12 @@ constexpr int kStageK = 128;   // K bytes per LDS stage of gemm_fp8_mx16_kernel
 // 32 (l / 16); the instruction pairs A and B by lane and byte, so this K order is as
 // good as any. The B tile goes in as the first operand, so a lane's 4 results are 4
 // consecutive n of row m = l % 16.
-template <class C, bool TAIL>
+template <class C, bool TAIL, bool BIAS>
 __global__ void __launch_bounds__(C::kThreads, 1)
 gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                      const float* __restrict__ sa, const float* __restrict__ sb,
-                     uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
-                     int tiles_n, int split_m, int split_n) {
+                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ D, int M, int N,
+                     int K, int M_valid, int tiles_m, int tiles_n, int split_m, int split_n) {
   static_assert(!C::BLOCK, "tensorwise only");
   constexpr int SB = (C::BM + C::BN) * kStageK;
   constexpr int kRowsPerInst = 1024 / kStageK;               // 8 rows of 128 bytes
@@ -684,6 +706,16 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // With an odd tile count per row, the last tile goes out on its own: 8 bytes (4
   // consecutive n) per lane.
   auto epilogue = [&](int m0, int n0) {
+    // BIAS: tile j's 4 columns of the lane are n0 + wn WTN + 16 j + 4 g .. + 3 (kept as
+    // packed bf16; columns past N read as 0)
+    uint2 bj[BIAS ? CT : 1];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        const int n = n0 + wn * C::WTN + 16 * j + 4 * g4;
+        bj[j] = n < N ? *reinterpret_cast<const uint2*>(bias + n) : make_uint2(0u, 0u);
+      }
+    }
     const int mrow = m0 + wm * C::WTM + r16;
     const int ncol = n0 + wn * C::WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
     const uint32_t base = ((uint32_t)mrow * (uint32_t)N + (uint32_t)ncol) * 2u;
@@ -693,13 +725,22 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
       const bool live = m < M_valid;   // rows past it are written as zeros, whatever
                                        // their sums hold (a select, not a product)
       const float si = scl;
+      // BIAS: the float32 bias of the lane's 4 columns of tile j, added after the scale
+      auto val = [&](int j, int r) {
+        if constexpr (BIAS) {
+          const uint32_t w = r < 2 ? bj[j].x : bj[j].y;
+          return acc[i][j][r] * si + __uint_as_float(r % 2 ? (w & 0xFFFF0000u) : (w << 16));
+        } else {
+          return acc[i][j][r] * si;
+        }
+      };
 #pragma unroll
       for (int jp = 0; jp < CT / 2; ++jp) {
         const int j = 2 * jp;
-        const uint32_t p0j = pack_bf16x2(acc[i][j][0] * si, acc[i][j][1] * si);
-        const uint32_t p1j = pack_bf16x2(acc[i][j][2] * si, acc[i][j][3] * si);
-        const uint32_t p0k = pack_bf16x2(acc[i][j + 1][0] * si, acc[i][j + 1][1] * si);
-        const uint32_t p1k = pack_bf16x2(acc[i][j + 1][2] * si, acc[i][j + 1][3] * si);
+        const uint32_t p0j = pack_bf16x2(val(j, 0), val(j, 1));
+        const uint32_t p1j = pack_bf16x2(val(j, 2), val(j, 3));
+        const uint32_t p0k = pack_bf16x2(val(j + 1, 0), val(j + 1, 1));
+        const uint32_t p1k = pack_bf16x2(val(j + 1, 2), val(j + 1, 3));
         const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
         const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
         v4i o = {(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
@@ -713,8 +754,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
         constexpr int j = CT - 1;
         typedef int v2i __attribute__((ext_vector_type(2)));
         const int n = n0 + wn * C::WTN + 16 * j + 4 * g4;
-        v2i o = {(int)pack_bf16x2(acc[i][j][0] * si, acc[i][j][1] * si),
-                 (int)pack_bf16x2(acc[i][j][2] * si, acc[i][j][3] * si)};
+        v2i o = {(int)pack_bf16x2(val(j, 0), val(j, 1)), (int)pack_bf16x2(val(j, 2), val(j, 3))};
         if (!live) o = v2i{0, 0};
         const uint32_t off =
             (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : kOutOfRange;
@@ -1141,8 +1181,8 @@ template <class C>
 __global__ void __launch_bounds__(C::kThreads, 1)
 gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                      const float* __restrict__ sa, const float* __restrict__ sb,
-                     uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
-                     int tiles_n) {
+                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ D, int M, int N,
+                     int K, int M_valid, int tiles_m, int tiles_n) {
   static_assert(!C::BLOCK, "tensorwise only");
   constexpr int SB = C::kStageBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t s0[SB];
@@ -1153,6 +1193,7 @@ gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 
   Tile<C> T;
   T.init(A, B, sa, sb, D, M, N, K, M_valid);
+  T.bias = bias;
   const int m0 = (blockIdx.x / tiles_n) * C::BM;
   const int n0 = (blockIdx.x % tiles_n) * C::BN;
   const auto tb = T.base(true, m0, n0);
@@ -1201,12 +1242,13 @@ int forced_cfg() {
 
 template <class C>
 hipError_t run_pipe(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
-                    uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
+                    const uint16_t* bias, uint16_t* D, int M, int N, int K, int M_valid,
+                    hipStream_t s) {
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + C::BN - 1) / C::BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   hipLaunchKernelGGL(gemm_fp8_pipe_kernel<C>, dim3((unsigned)tiles), dim3(C::kThreads), 0, s, A,
-                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n);
+                     B, sa, sb, bias, D, M, N, K, M_valid, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -1215,7 +1257,8 @@ constexpr int kMaxWorkgroups = 256;
 
 template <class C>
 hipError_t run_persist(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
-                       uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
+                       const uint16_t* bias, uint16_t* D, int M, int N, int K, int M_valid,
+                       hipStream_t s) {
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + C::BN - 1) / C::BN;
   const int tiles = tiles_m * tiles_n;
@@ -1233,7 +1276,7 @@ hipError_t run_persist(const uint8_t* A, const uint8_t* B, const float* sa, cons
     }
   }
   hipLaunchKernelGGL(gemm_fp8_persist_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
-                     B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+                     B, sa, sb, bias, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   return hipGetLastError();
 }
 
@@ -1259,7 +1302,8 @@ template <int BROWS> using Blk2 =
 
 template <class C>
 hipError_t run_mx16(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
-                    uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
+                    const uint16_t* bias, uint16_t* D, int M, int N, int K, int M_valid,
+                    hipStream_t s) {
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + C::BN - 1) / C::BN;
   const int tiles = tiles_m * tiles_n;
@@ -1275,22 +1319,31 @@ hipError_t run_mx16(const uint8_t* A, const uint8_t* B, const float* sa, const f
       if (cost < best) { best = cost; split_m = pm; split_n = pn; }
     }
   }
-  if (K % (2 * kStageK) == 0)
-    hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, false>), dim3((unsigned)grid), dim3(C::kThreads),
-                       0, s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  const dim3 g((unsigned)grid), b(C::kThreads);
+  const bool tail = K % (2 * kStageK) != 0;
+  if (bias == nullptr && !tail)
+    hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, false, false>), g, b, 0, s, A, B, sa, sb, bias, D,
+                       M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  else if (bias == nullptr)
+    hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, true, false>), g, b, 0, s, A, B, sa, sb, bias, D,
+                       M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  else if (!tail)
+    hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, false, true>), g, b, 0, s, A, B, sa, sb, bias, D,
+                       M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   else
-    hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, true>), dim3((unsigned)grid), dim3(C::kThreads),
-                       0, s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+    hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, true, true>), g, b, 0, s, A, B, sa, sb, bias, D,
+                       M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   return hipGetLastError();
 }
 
 template <class C4, class C2>
 hipError_t run_tensorwise(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
-                          uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
+                          const uint16_t* bias, uint16_t* D, int M, int N, int K, int M_valid,
+                          hipStream_t s) {
   const int nk = (K + kBKS - 1) / kBKS;
-  if (nk % 4 == 0) return run_persist<C4>(A, B, sa, sb, D, M, N, K, M_valid, s);
-  if (nk % 2 == 0) return run_persist<C2>(A, B, sa, sb, D, M, N, K, M_valid, s);
-  return run_pipe<C2>(A, B, sa, sb, D, M, N, K, M_valid, s);
+  if (nk % 4 == 0) return run_persist<C4>(A, B, sa, sb, bias, D, M, N, K, M_valid, s);
+  if (nk % 2 == 0) return run_persist<C2>(A, B, sa, sb, bias, D, M, N, K, M_valid, s);
+  return run_pipe<C2>(A, B, sa, sb, bias, D, M, N, K, M_valid, s);
 }
 
 template <class C>
@@ -1336,18 +1389,24 @@ hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const 
     return run_mx16b<BlkMx16<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
   const int nk = K / kBKS;
   if constexpr (BROWS != 1)
-    if (nk % 4 == 0) return run_persist<Blk4<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
-  return run_persist<Blk2<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
+    if (nk % 4 == 0)
+      return run_persist<Blk4<BROWS>>(A, B, sa, sb, nullptr, D, M, N, K, M_valid, s);
+  return run_persist<Blk2<BROWS>>(A, B, sa, sb, nullptr, D, M, N, K, M_valid, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
-                           uint16_t* D, int64_t M, int64_t N, int64_t K, int64_t M_valid,
-                           bool block_scaled, int b_rows_per_scale, hipStream_t s) {
+                           const uint16_t* bias, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                           int64_t M_valid, bool block_scaled, int b_rows_per_scale,
+                           hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
-  // an empty contraction (e.g. a weight gradient over no tokens): every sum is +0
-  if (K == 0) return launch_fill_u32(reinterpret_cast<uint32_t*>(D), 0u, M * N / 2, s);
+  // an empty contraction (e.g. a weight gradient over no tokens): every sum is +0, so the
+  // valid rows hold the bias (if any)
+  if (K == 0) {
+    if (bias != nullptr) return launch_bias_rows(bias, D, M, N, M_valid, s);
+    return launch_fill_u32(reinterpret_cast<uint32_t*>(D), 0u, M * N / 2, s);
+  }
   const int m = (int)M, n = (int)N, k = (int)K, mv = (int)M_valid;
   if (block_scaled) {
     if (b_rows_per_scale == 1) return run_block<1>(A, B, sa, sb, D, m, n, k, mv, s);
@@ -1371,13 +1430,14 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, 
     };
     const int64_t c0 = cost(256, 256), cm = cost(224, 256), cn = cost(256, 224);
     if (c0 > 256 * 256) {
-      if (cm < c0 && cm <= cn) return run_mx16<TwMx16M224>(A, B, sa, sb, D, m, n, k, mv, s);
-      if (cn < c0) return run_mx16<TwMx16N224>(A, B, sa, sb, D, m, n, k, mv, s);
+      if (cm < c0 && cm <= cn)
+        return run_mx16<TwMx16M224>(A, B, sa, sb, bias, D, m, n, k, mv, s);
+      if (cn < c0) return run_mx16<TwMx16N224>(A, B, sa, sb, bias, D, m, n, k, mv, s);
     }
-    return run_mx16<TwMx16>(A, B, sa, sb, D, m, n, k, mv, s);
+    return run_mx16<TwMx16>(A, B, sa, sb, bias, D, m, n, k, mv, s);
   }
-  if (cfg == 1) return run_tensorwise<TwSmall, TwSmall2>(A, B, sa, sb, D, m, n, k, mv, s);
-  return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, D, m, n, k, mv, s);
+  if (cfg == 1) return run_tensorwise<TwSmall, TwSmall2>(A, B, sa, sb, bias, D, m, n, k, mv, s);
+  return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, bias, D, m, n, k, mv, s);
 }
 
 }  // namespace fp8lin

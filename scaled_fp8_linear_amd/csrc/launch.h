@@ -29,11 +29,21 @@ hipError_t launch_scale_update(int mode, float* amax, bool clear_amax, float* hi
 hipError_t launch_pad_tokens(const uint16_t* x, int64_t T, int64_t cols, int64_t T_pad,
                              uint16_t* x_pad, hipStream_t s);
 
-// D[m,n] = bf16(scale * sum_k A[m,k] * B[n,k]); A [M,K], B [N,K], D [M,N].
-// Tensorwise: scale = sa[0] * sb[0]. Block: sa [M, K/128]; sb [N/b_rows, K/128]
-// with b_rows = 128 (weight tiles) or 1 (1x128 tiles). Rows m >= M_valid of D are 0.
+// D[m,n] = bf16(scale * sum_k A[m,k] * B[n,k] (+ bias[n])); A [M,K], B [N,K], D [M,N].
+// Tensorwise: scale = sa[0] * sb[0]; bias bf16 [N] or nullptr. Block: sa [M, K/128];
+// sb [N/b_rows, K/128] with b_rows = 128 (weight tiles) or 1 (1x128 tiles); no bias.
+// Rows m >= M_valid of D are 0.
 hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
-                           uint16_t* D, int64_t M, int64_t N, int64_t K, int64_t M_valid,
-                           bool block_scaled, int b_rows_per_scale, hipStream_t s);
+                           const uint16_t* bias, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                           int64_t M_valid, bool block_scaled, int b_rows_per_scale,
+                           hipStream_t s);
+
+// D[m, :] = bias for m < M_valid, 0 below (the output of an empty contraction with bias).
+hipError_t launch_bias_rows(const uint16_t* bias, uint16_t* D, int64_t M, int64_t N,
+                            int64_t M_valid, hipStream_t s);
+
+// db[c] = bf16(sum over r < rows_valid of g[r, c]), float32 sums in a fixed order.
+hipError_t launch_bias_grad(const uint16_t* g, int64_t rows, int64_t cols, int64_t rows_valid,
+                            uint16_t* db, hipStream_t s);
 
 }  // namespace fp8lin

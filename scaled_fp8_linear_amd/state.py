@@ -91,7 +91,7 @@ class DelayedScalingLinear:
             return True
         return False
 
-    def forward(self, x, w, rows_valid=None, out=None, bufs=None, stream=None):
+    def forward(self, x, w, rows_valid=None, out=None, bufs=None, stream=None, bias=None):
         """y = x W^T. ``bufs`` may hold preallocated qw, qw_t, qx, qx_t tensors."""
         b = bufs or {}
         p = self.probe
@@ -110,7 +110,7 @@ class DelayedScalingLinear:
                 amax=self.amax_x, amax_accumulate=self.acc, stream=stream)
         with p("gemm"):
             y = _abi.fp8_linear_fwd(qx, qw, sx, self.w_scale, y=out, M_valid=rows_valid,
-                                    stream=stream)
+                                    stream=stream, bias=bias)
         with p("scale"):
             _abi.fp8_scale_update(_abi.FP8_SCALE_FROM_AMAX, amax=self.amax_x,
                                   scale=Slot(self.x_scale, self.nxt),

@@ -8,6 +8,7 @@ import pytest
 
 import workloads
 from oracle import gemm
+from oracle.bias import add_bias, bias_bound, bias_grad, bias_grad_bound
 from oracle.linear import DelayedLinear
 from tests.gpu_util import assert_within, dev_bf16, f32_bits, host_bf16_f64, note
 
@@ -145,5 +146,42 @@ def test_step_without_backward(lib):
         b = ref.backward(d["g"])
         assert_within(host_bf16_f64(xd.grad), b["dx"],
                       gemm.error_bound(b["qg"], f["qw_t"], b["sg"], f["sw"]), f"dx step {t}")
+        _scales_equal(layer._lin.state(), ref.state(), f"step {t}")
+    lib.fp8_state().reset()
+
+
+@pytest.mark.parametrize("M", [256, 250])
+def test_module_with_bias(lib, M):
+    """Fp8Linear(bias=True): y = x W^T + b through the bias epilogue, db the column sum of
+    the output gradient over the valid tokens; 3 steps against the oracle."""
+    K, N = 256, 384
+    lib.fp8_state().reset()
+    layer = lib.Fp8Linear(K, N, bias=True, device="cuda")
+    ref = DelayedLinear()
+    Mp = M + (-M) % 16
+    for t in (1, 2, 3):
+        d = workloads.linear_inputs(2, t, M=Mp, K=K, N=N)
+        x, g, w = d["x"][:M], d["g"][:M], d["w"]
+        bias = workloads.bf16_tensor("normal", (N,), 2, 99, t, std=0.1)
+        note(f"Fp8Linear with bias, step {t}, M={M}")
+        layer.weight.data.copy_(dev_bf16(w))
+        layer.bias.data.copy_(dev_bf16(bias))
+        layer.weight.grad = None
+        layer.bias.grad = None
+        xd = dev_bf16(x).requires_grad_(True)
+        with lib.fp8_autocast():
+            y = layer(xd)
+        y.backward(dev_bf16(g))
+        torch.cuda.synchronize()
+        ref.begin_step()
+        f = ref.forward(_pad(x, Mp), w, rows_valid=M)
+        b = ref.backward(_pad(g, Mp))
+        want = add_bias(f["y"][:M], bias)
+        bound = gemm.error_bound(f["qx"], f["qw"], f["sx"], f["sw"])[:M] + bias_bound(bias)[None, :]
+        assert_within(host_bf16_f64(y), want, bound, f"y step {t}")
+        assert_within(host_bf16_f64(layer.bias.grad), bias_grad(_pad(g, Mp), M),
+                      bias_grad_bound(_pad(g, Mp), M), f"db step {t}")
+        assert_within(host_bf16_f64(xd.grad), b["dx"][:M],
+                      gemm.error_bound(b["qg"], f["qw_t"], b["sg"], f["sw"])[:M], f"dx step {t}")
         _scales_equal(layer._lin.state(), ref.state(), f"step {t}")
     lib.fp8_state().reset()
