@@ -28,12 +28,13 @@ namespace fp8lin {
 
 namespace {
 
-// Tile of TR rows x TC columns per workgroup of THREADS lanes; NT: streaming
-// (non-temporal) memory accesses.
-template <int TR, int TC, int THREADS, bool NT>
+// Tile of TR rows x TC columns per workgroup of THREADS lanes. NT selects
+// streaming (non-temporal) accesses per stream: bit 0 the bf16 loads, bit 1 the
+// q stores, bit 2 the q_t stores.
+template <int TR, int TC, int THREADS, int NT>
 struct QCfg {
   static constexpr int kQTR = TR, kQTC = TC, kQThreads = THREADS;
-  static constexpr bool kNT = NT;
+  static constexpr int kNT = NT;
   static constexpr int kColDwords = TR / 4;          // dwords per transposed column piece
   static constexpr int kChunks = TC / 8;             // 8-column chunks per tile row
   static constexpr int kGroups = THREADS / kChunks;  // 4-row groups per pass
@@ -50,19 +51,19 @@ __device__ __forceinline__ int lds_slot(int c, int i) {
   return c * COLDW + (i ^ ((c >> 3) & (COLDW - 1)));
 }
 
-template <bool NT>
+template <int NT>
 __device__ __forceinline__ uint4 ld16(const void* p) {
-  if constexpr (NT) return ld_stream16(p);
+  if constexpr ((NT & 1) != 0) return ld_stream16(p);
   else return *reinterpret_cast<const uint4*>(p);
 }
-template <bool NT>
+template <int NT>
 __device__ __forceinline__ void st16(void* p, uint4 v) {
-  if constexpr (NT) st_stream16(p, v);
+  if constexpr ((NT & 4) != 0) st_stream16(p, v);
   else *reinterpret_cast<uint4*>(p) = v;
 }
-template <bool NT>
+template <int NT>
 __device__ __forceinline__ void st8(void* p, uint32_t a, uint32_t b) {
-  if constexpr (NT) st_stream8(p, a, b);
+  if constexpr ((NT & 2) != 0) st_stream8(p, a, b);
   else *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
 }
 
@@ -74,7 +75,7 @@ quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t
                            uint32_t* __restrict__ amax_bits, int64_t tiles_c) {
   constexpr int kQTR = QC::kQTR, kQTC = QC::kQTC, kQThreads = QC::kQThreads;
   constexpr int kColDwords = QC::kColDwords;
-  constexpr bool NT = QC::kNT;
+  constexpr int NT = QC::kNT;
   __shared__ uint32_t tile_t[kQTC * kColDwords];
   __shared__ uint32_t wave_max[kQThreads / 64];
 
@@ -258,19 +259,17 @@ hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t rows, int64_t c
       return e;
     return hipSuccess;
   }
+  // Default: streaming loads and q stores, ordinary q_t stores. q_t leaves as 128-byte
+  // pieces of rows that lie `rows` bytes apart; streaming stores send each piece to
+  // HBM alone, which costs a third of the rate on tall tensors (54672 x 4096: 3.4
+  // against 4.7 TB/s), while the cached path merges neighbouring pieces first.
   switch (quant_cfg()) {
-    case 1: return run_q<QCfg<128, 256, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 2: return run_q<QCfg<64, 512, 256, true>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 3: return run_q<QCfg<64, 512, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 4: return run_q<QCfg<128, 512, 512, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 5: return run_q<QCfg<64, 256, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 6: return run_q<QCfg<128, 128, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 7: return run_q<QCfg<256, 256, 512, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 8: return run_q<QCfg<256, 512, 1024, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 9: return run_q<QCfg<128, 512, 512, true>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 10: return run_q<QCfg<256, 256, 512, true>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 11: return run_q<QCfg<256, 128, 256, false>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    default: return run_q<QCfg<128, 256, 256, true>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 1: return run_q<QCfg<128, 256, 256, 7>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 2: return run_q<QCfg<128, 256, 256, 0>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 3: return run_q<QCfg<256, 256, 512, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 4: return run_q<QCfg<128, 512, 512, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 5: return run_q<QCfg<128, 256, 256, 2>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    default: return run_q<QCfg<128, 256, 256, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
   }
 }
 

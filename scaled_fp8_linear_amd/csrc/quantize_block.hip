@@ -14,7 +14,8 @@
 //    index that wgrad contracts over), reduced over the 16 row groups;
 //  * 128x128 mode: one scale for the whole tile; q_t is q transposed.
 // The transposed codes go through LDS (4-row dword pieces, XOR-swizzled) and
-// leave with 16-byte stores, as in the tensorwise pass.
+// leave with 16-byte stores, as in the tensorwise pass; as there, the loads and
+// the q stores stream (non-temporal) and the q_t stores take the cached path.
 #include "common.h"
 #include "launch.h"
 
@@ -86,7 +87,7 @@ quantize_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
   for (int i = 0; i < 8; ++i) {
     const int64_t r = row0 + 8 * rg + i;
     ok[i] = r < rows_valid;
-    v[i] = ok[i] ? *reinterpret_cast<const uint4*>(x + r * cols + col) : make_uint4(0, 0, 0, 0);
+    v[i] = ok[i] ? ld_stream16(x + r * cols + col) : make_uint4(0, 0, 0, 0);
   }
 
   // ---- per-row maxima (row tiles), per-column maxima (column tiles)
@@ -182,7 +183,7 @@ quantize_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
       uint32_t lo = codes4(v[i].x, v[i].y, s, s, s, s);
       uint32_t hi = codes4(v[i].z, v[i].w, s, s, s, s);
       if (!ok[i]) { lo = 0u; hi = 0u; }
-      if (r < rows) *reinterpret_cast<uint2*>(q + r * cols + col) = make_uint2(lo, hi);
+      if (r < rows) st_stream8(q + r * cols + col, lo, hi);
     }
   }
   if (q_t == nullptr) return;
