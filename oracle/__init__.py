@@ -19,11 +19,13 @@ Sources (the web pages this method is taken from):
 * NeMo PR 15754, "Add FP8 support for SALMAutomodel", review thread on BSHD
   padding: ``pad = (-T) % seq_multiple``; TE's block recipe.
 * The OCP 8-bit floating point specification (OFP8, E4M3 variant), which the
-  name "e4m3" and the maximum 448 identify.
+  name "e4m3" and the maximum 448 identify; its E5M2 variant for the hybrid
+  format's gradients.
 
 Modules:
 
 * ``e4m3``      -- the E4M3 code table and two independent encoders.
+* ``e5m2``      -- the same for E5M2, the gradient format of the hybrid recipe.
 * ``quantize``  -- tensorwise quantize with amax, and the transposed copy.
 * ``scaling``   -- scale from amax, the weight amax-history ring, and the
                    per-step delayed-scaling schedule of one linear layer.

@@ -24,13 +24,19 @@ from . import block as blk
 from .gemm import scaled_gemm
 from .quantize import amax as amax_of
 from .quantize import quantize_tensorwise
-from .scaling import StepCounter, WeightMeta, scale_from_amax
+from .scaling import E4M3_MAX, E5M2_MAX, StepCounter, WeightMeta, scale_from_amax
 
 
 class DelayedLinear:
-    """``FP8TensorMeta`` of one weight plus its activation/gradient scales."""
+    """``FP8TensorMeta`` of one weight plus its activation/gradient scales.
 
-    def __init__(self, update_interval: int = 16):
+    ``grad_format`` "e5m2" is the hybrid format: g is coded in E5M2 with scales
+    from 57344 instead of 448, and dgrad/wgrad take it as their first operand;
+    x and W stay E4M3."""
+
+    def __init__(self, update_interval: int = 16, grad_format: str = "e4m3"):
+        assert grad_format in ("e4m3", "e5m2")
+        self.grad_format = grad_format
         self.counter = StepCounter(update_interval)
         self.w = WeightMeta(update_interval)
         self.x_scale = np.float32(1.0)
@@ -64,10 +70,11 @@ class DelayedLinear:
         s = self._saved
         rv = s["rv"]
         sg, sg_inv = self.g_scale, self.g_scale_inv
-        qg, qg_t, amax_g = quantize_tensorwise(g_bits, sg_inv, rv)
-        dx = scaled_gemm(qg, s["qw_t"], sg, s["sw"])
+        gf = self.grad_format
+        qg, qg_t, amax_g = quantize_tensorwise(g_bits, sg_inv, rv, gf)
+        dx = scaled_gemm(qg, s["qw_t"], sg, s["sw"], gf)
         dx[rv:] = 0.0
-        dw = scaled_gemm(qg_t, s["qx_t"], sg, s["sx"])
+        dw = scaled_gemm(qg_t, s["qx_t"], sg, s["sx"], gf)
         self._finish_backward(amax_g)
         return dict(dx=dx, dw=dw, qg=qg, qg_t=qg_t, amax_g=amax_g, sg=sg, sg_inv=sg_inv)
 
@@ -78,7 +85,8 @@ class DelayedLinear:
 
     def _finish_backward(self, amax_g) -> None:
         """After the backward: delay the gradient scale."""
-        self.g_scale, self.g_scale_inv = scale_from_amax(amax_g)
+        fmax = E5M2_MAX if self.grad_format == "e5m2" else E4M3_MAX
+        self.g_scale, self.g_scale_inv = scale_from_amax(amax_g, fmax)
 
     def scales_only_step(self, x_bits, w_bits, g_bits, rows_valid=None) -> dict:
         """The same bookkeeping as forward + backward without the GEMMs (for long runs at

@@ -21,6 +21,9 @@ So, for a bf16 tensor X and the float32 multiplier ``scale_inv``:
   exact, so the maximum is exact; it is 0 for an all-zero input and NaN if any
   valid element is NaN (reading: NaN propagates, as ``torch.max`` does).
 
+The gradients of the hybrid format are coded in E5M2 (``oracle.e5m2``) by
+the same steps, with the multiplier 57344/amax.
+
 Rows ``r >= rows_valid`` are padding (NeMo PR 15754 review thread: tokens
 appended by ``pad = (-T) % seq_multiple``): they are not read, do not enter
 amax, and their codes are written as 0x00.
@@ -29,7 +32,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, e5m2
+
+CODECS = {"e4m3": e4m3, "e5m2": e5m2}
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -47,30 +52,33 @@ def amax(x_bits: np.ndarray, rows_valid: int | None = None) -> np.float32:
     return np.float32(np.max(np.abs(x)))
 
 
-def encode_product(x: np.ndarray, v: np.ndarray) -> np.ndarray:
+def encode_product(x: np.ndarray, v: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
     """Codes of the float32 products ``v`` of inputs ``x`` (float32, same shape):
-    the E4M3 encoder, except that a NaN product takes the sign of its input."""
-    code = e4m3.encode(v)
-    nan_code = np.where(np.signbit(x), e4m3.NAN_CODE | e4m3.SIGN_BIT, e4m3.NAN_CODE)
+    the format's encoder, except that a NaN product takes the sign of its input."""
+    codec = CODECS[fmt]
+    code = codec.encode(v)
+    nan_code = np.where(np.signbit(x), codec.NAN_CODE | codec.SIGN_BIT, codec.NAN_CODE)
     return np.where(np.isnan(v), nan_code, code).astype(np.uint8)
 
 
-def quantize_values(x_bits: np.ndarray, scale_inv) -> np.ndarray:
-    """e4m3 codes of float32(x) * scale_inv, elementwise, any shape."""
+def quantize_values(x_bits: np.ndarray, scale_inv, fmt: str = "e4m3") -> np.ndarray:
+    """Codes (``fmt`` "e4m3" or "e5m2") of float32(x) * scale_inv, elementwise."""
     x = bf16_to_f32(x_bits)
     with np.errstate(invalid="ignore", over="ignore"):
         v = x * np.float32(scale_inv)            # float32 * float32 -> float32 (RNE)
-    return encode_product(x, v)
+    return encode_product(x, v, fmt)
 
 
-def quantize_tensorwise(x_bits: np.ndarray, scale_inv, rows_valid: int | None = None):
+def quantize_tensorwise(x_bits: np.ndarray, scale_inv, rows_valid: int | None = None,
+                        fmt: str = "e4m3"):
     """Return ``(q, q_t, amax)`` for a bf16 [rows, cols] tensor.
 
-    ``q`` is uint8 [rows, cols], ``q_t`` uint8 [cols, rows], ``amax`` float32.
+    ``q`` is uint8 [rows, cols], ``q_t`` uint8 [cols, rows], ``amax`` float32;
+    ``fmt`` "e5m2" codes the hybrid format's gradients.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     rows = x_bits.shape[0]
     rv = rows if rows_valid is None else int(rows_valid)
     q = np.zeros(x_bits.shape, dtype=np.uint8)
-    q[:rv] = quantize_values(x_bits[:rv], scale_inv)
+    q[:rv] = quantize_values(x_bits[:rv], scale_inv, fmt)
     return q, np.ascontiguousarray(q.T), amax(x_bits, rv)

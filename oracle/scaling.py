@@ -31,18 +31,21 @@ from __future__ import annotations
 import numpy as np
 
 E4M3_MAX = np.float32(448.0)
+E5M2_MAX = np.float32(57344.0)   # gradients in the hybrid format: the E5M2 maximum
 AMAX_FLOOR = np.float32(1e-12)
 UPDATE_INTERVAL = 16
 
 
-def scale_from_amax(amax) -> tuple[np.float32, np.float32]:
-    """``_update_delayed_scale``: (scale, scale_inv) from one amax value."""
+def scale_from_amax(amax, fmax=E4M3_MAX) -> tuple[np.float32, np.float32]:
+    """``_update_delayed_scale``: (scale, scale_inv) from one amax value.
+    ``fmax`` is the format's largest value: 448, or 57344 for E5M2 gradients."""
     a = np.float32(amax)
+    fmax = np.float32(fmax)
     if not np.isnan(a) and a < AMAX_FLOOR:
         a = AMAX_FLOOR
     with np.errstate(invalid="ignore", divide="ignore"):
-        scale = np.float32(a / E4M3_MAX)
-        scale_inv = np.float32(E4M3_MAX / a)
+        scale = np.float32(a / fmax)
+        scale_inv = np.float32(fmax / a)
     return scale, scale_inv
 
 

@@ -158,3 +158,40 @@ def test_nan_products_take_the_input_sign():
     # inf * 0 is NaN as well
     z = np.array([0x7F80, 0xFF80], np.uint16)
     assert list(quantize_values(z, np.float32(0.0))) == [0x7F, 0xFF]
+
+
+def test_mixed_format_gemm_against_python_integers():
+    """E5M2 first operand: every E5M2 value times 2**16 and every E4M3 value times
+    2**9 is an integer, so the exact sum is an integer over 2**25. At K = 8 the
+    float64 product is exact; at K = 96 it is within K * 2**-52 * sum |a b|."""
+    from oracle import e5m2
+    rng = np.random.default_rng(3)
+    for K, exact_fp64 in ((8, True), (96, False)):
+        qa = rng.integers(0, 0x7C, size=(6, K)).astype(np.uint8)     # finite E5M2 codes
+        qa[rng.random(qa.shape) < 0.5] |= 0x80
+        qb = rng.integers(0, 0x7F, size=(5, K)).astype(np.uint8)     # finite E4M3 codes
+        qb[rng.random(qb.shape) < 0.5] |= 0x80
+        S = gemm.unscaled_product(qa, qb, a_fmt="e5m2")
+        D = gemm.scaled_gemm(qa, qb, 0.25, 3.0, a_fmt="e5m2")
+        for m in range(6):
+            for n in range(5):
+                terms = [int(e5m2.decode_code(qa[m, k]) * 65536) *
+                         int(e4m3.decode_code(qb[n, k]) * 512) for k in range(K)]
+                acc = sum(terms)
+                mag = sum(abs(t) for t in terms) / float(1 << 25)
+                if exact_fp64:
+                    assert S[m, n] == acc / float(1 << 25)
+                else:
+                    assert abs(S[m, n] - acc / float(1 << 25)) <= K * 2.0 ** -52 * mag
+                assert D[m, n] == S[m, n] * 0.75
+        # the E5M2 operand is really decoded as E5M2: 0x3C is 1.0 there, 1.5 in E4M3
+        one = gemm.unscaled_product(np.full((1, 1), 0x3C, np.uint8),
+                                    np.full((1, 1), 0x38, np.uint8), a_fmt="e5m2")
+        assert one[0, 0] == 1.0
+
+
+def test_mixed_format_error_bound_uses_e5m2_norms():
+    qa = np.array([[0x3C, 0x40]], np.uint8)        # E5M2: 1, 2
+    qb = np.array([[0x38, 0x38]], np.uint8)        # E4M3: 1, 1
+    b = gemm.error_bound(qa, qb, 1.0, 1.0, a_fmt="e5m2")
+    assert b[0, 0] == pytest.approx(1e-2 * np.sqrt(5.0) * np.sqrt(2.0), rel=1e-15)

@@ -76,3 +76,27 @@ def test_block_linear_matches_autograd():
     _close(r["dw"], gdq_t @ xdq_t.T)
     _, _, dw_ref = _autograd(xdq_t.T, wdq, gdq_t.T)
     _close(r["dw"], dw_ref)
+
+
+def test_hybrid_format_linear_matches_autograd():
+    """E5M2 gradients: the gradient scale comes from 57344 and dgrad/wgrad decode
+    Qg and Qg^T as E5M2."""
+    from oracle import e5m2, scaling
+    lin = DelayedLinear(grad_format="e5m2")
+    for step in range(3):
+        d = workloads.linear_inputs(2, step, M=48, K=64, N=32)
+        lin.begin_step()
+        f = lin.forward(d["x"], d["w"], rows_valid=40)
+        b = lin.backward(d["g"])
+        xdq = e4m3.decode(f["qx"]) * np.float64(f["sx"])
+        wdq = e4m3.decode(f["qw"]) * np.float64(f["sw"])
+        gdq = e5m2.decode(b["qg"]) * np.float64(b["sg"])
+        y, dx, dw = _autograd(xdq, wdq, gdq)
+        y[40:] = 0.0
+        dx[40:] = 0.0
+        _close(f["y"], y)
+        _close(b["dx"], dx)
+        _close(b["dw"], dw)
+        # the next gradient scale is amax/57344 (one step late)
+        assert lin.g_scale == scaling.scale_from_amax(b["amax_g"], 57344.0)[0]
+        assert np.all(b["qg"][40:] == 0)
