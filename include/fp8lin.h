@@ -84,6 +84,23 @@ enum {
 };
 
 /*
+ * The hybrid format: gradients coded in OCP E5M2 (sign, 5 exponent bits with
+ * bias 15, 2 mantissa bits; largest finite value 57344 = 0x7B; 0x7C is
+ * infinity and 0x7D..0x7F NaN), activations and weights in E4M3. E5M2 trades
+ * one mantissa bit for a range of 2^-16 .. 57344. The pages name E4M3 only;
+ * this is the e5m2 gradient variant the same TE-style design allows, run on
+ * gfx950's mixed-format FP8 matrix instructions.
+ */
+enum {
+  FP8_E5M2 = 0x200,   /* fp8_quantize_amax (TENSORWISE): emit E5M2 codes, scale_inv
+                         being 57344/amax; fp8_scale_update (FROM_AMAX, REFRESH):
+                         the format maximum is 57344 instead of 448            */
+  FP8_A_E5M2 = 0x200  /* fp8_linear_fwd/dgrad/wgrad (TENSORWISE, no bias): the
+                         FIRST operand (x, g or g^T) holds E5M2 codes; the second
+                         stays E4M3                                            */
+};
+
+/*
  * fp8_quantize_amax -- fused bf16 -> e4m3 quantize with its amax, emitting
  * the row-major codes and their transpose in one pass over x.
  *
@@ -112,6 +129,10 @@ enum {
  *              NaN). Computed on the same pass. With FP8_AMAX_ACCUMULATE in
  *              gran it becomes max(amax[0], that maximum) instead.
  *   scale, scale_t  must be NULL.
+ *   With FP8_E5M2 in gran the codes are OCP E5M2 instead: the same float32
+ *   product, round to nearest even on the E5M2 grid (subnormals down to
+ *   2^-16 kept), saturating to +-57344 (also for +-inf); a NaN product gives
+ *   0x7F with its input's sign.
  *
  * FP8_BLOCK_1x128 (activations, gradients; current per-tile scaling):
  *   scale_inv  must be NULL (each tile's multiplier is computed in the pass
@@ -158,6 +179,8 @@ int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_va
  *   caller refreshes when its step counter reaches a multiple of 16.
  * FP8_SCALE_CLEAR_AMAX (flag, FROM_AMAX and RECORD): amax[0] is set to +0
  *   after it is read, ready for a FP8_AMAX_ACCUMULATE quantize pass.
+ * FP8_E5M2 (flag, FROM_AMAX and REFRESH): 57344 replaces 448 in both
+ *   divisions, for a tensor coded in E5M2.
  *
  * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE (len < 1, pos out of range, bad mode
  * -> FP8_ERR_UNSUPPORTED), FP8_ERR_HIP.
@@ -179,7 +202,9 @@ int fp8_scale_update(int mode, float* amax, float* hist, int32_t len, int32_t po
  *   FP8_BLOCK_1x128 (the block recipe): sx [M, K/128], sw [N/128, K/128];
  *       the scales multiply each 128-wide partial sum.
  *   M, N, K multiples of 16 (K, N multiples of 128 in the block recipe);
- *   0 <= M_valid <= M. K = 0 (an empty sum) writes +0 everywhere and reads
+ *   0 <= M_valid <= M. FP8_A_E5M2 OR-ed into gran (FP8_TENSORWISE only): the
+ *   first operand holds E5M2 codes (the same for dgrad's qg and wgrad's qg_t,
+ *   the hybrid format's gradients). K = 0 (an empty sum) writes +0 everywhere and reads
  *   neither operands nor scales, which may then be NULL (the same holds for
  *   the contraction size of dgrad and wgrad).
  */

@@ -6,7 +6,7 @@ declared in ``include/fp8lin.h``); this package is its thin Python binding
 used for device memory and streams only. Importing works without the built
 library; calling any entry point without it raises.
 """
-from ._abi import (FP8_AMAX_ACCUMULATE, FP8_BLOCK_1x128, FP8_BLOCK_128x128, FP8_SCALE_CLEAR_AMAX,
+from ._abi import (FP8_A_E5M2, FP8_AMAX_ACCUMULATE, FP8_BLOCK_1x128, FP8_E5M2, FP8_BLOCK_128x128, FP8_SCALE_CLEAR_AMAX,
                    FP8_SCALE_FROM_AMAX, FP8_SCALE_RECORD, FP8_SCALE_REFRESH, FP8_TENSORWISE,
                    Fp8Error, Slot, fp8_bias_grad, fp8_last_error,
                    fp8_linear_dgrad, fp8_linear_fwd, fp8_linear_wgrad, fp8_pad_tokens,
@@ -19,5 +19,6 @@ __all__ = ["fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linea
            "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version", "load",
            "Fp8Error", "Slot", "DelayedScalingLinear", "FP8_TENSORWISE", "FP8_BLOCK_1x128",
            "FP8_BLOCK_128x128", "FP8_SCALE_FROM_AMAX", "FP8_SCALE_RECORD", "FP8_SCALE_REFRESH",
-           "FP8_AMAX_ACCUMULATE", "FP8_SCALE_CLEAR_AMAX", "Fp8Linear", "fp8_autocast",
+           "FP8_AMAX_ACCUMULATE", "FP8_SCALE_CLEAR_AMAX", "FP8_E5M2", "FP8_A_E5M2",
+           "Fp8Linear", "fp8_autocast",
            "fp8_state"]

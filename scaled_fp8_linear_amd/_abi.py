@@ -21,6 +21,8 @@ FP8_TENSORWISE, FP8_BLOCK_1x128, FP8_BLOCK_128x128 = 0, 1, 2
 FP8_SCALE_FROM_AMAX, FP8_SCALE_RECORD, FP8_SCALE_REFRESH = 0, 1, 2
 FP8_AMAX_ACCUMULATE = 0x100     # flag for fp8_quantize_amax (tensorwise)
 FP8_SCALE_CLEAR_AMAX = 0x100    # flag for fp8_scale_update (FROM_AMAX, RECORD)
+FP8_E5M2 = 0x200                # flag: E5M2 codes (quantize), 57344 as format max (scale update)
+FP8_A_E5M2 = 0x200              # flag for the GEMMs: the first operand holds E5M2 codes
 
 EXPORTS = ("fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
            "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version",
@@ -134,12 +136,12 @@ def _fptr(v, name):
 
 def fp8_quantize_amax(x, rows_valid=None, gran=FP8_TENSORWISE, scale_inv=None, q=None, q_t=None,
                       amax=None, scale=None, scale_t=None, want_q=True, want_q_t=True,
-                      want_amax=True, amax_accumulate=False, stream=None):
+                      want_amax=True, amax_accumulate=False, e5m2=False, stream=None):
     """Quantize a bf16 [rows, cols] tensor. Returns (q, q_t, amax, scale, scale_t).
 
     Outputs that are not passed in are allocated here (``want_*`` False skips them).
     ``amax_accumulate`` (tensorwise): fold max|x| into the given ``amax`` instead of
-    overwriting it.
+    overwriting it. ``e5m2`` (tensorwise): E5M2 codes instead of E4M3.
     """
     if amax_accumulate and amax is None:
         raise ValueError("amax_accumulate needs the amax tensor to fold into")
@@ -167,25 +169,30 @@ def fp8_quantize_amax(x, rows_valid=None, gran=FP8_TENSORWISE, scale_inv=None, q
                                   dtype=torch.float32, device=dev)
     q, q_t = _codes(q), _codes(q_t)
     _check("fp8_quantize_amax", load().fp8_quantize_amax(
-        _ptr(x), rows, cols, rv, gran | (FP8_AMAX_ACCUMULATE if amax_accumulate else 0),
+        _ptr(x), rows, cols, rv,
+        gran | (FP8_AMAX_ACCUMULATE if amax_accumulate else 0) | (FP8_E5M2 if e5m2 else 0),
         _fptr(scale_inv, "scale_inv"), _ptr(q), _ptr(q_t),
         _fptr(amax, "amax"), _fptr(scale, "scale"), _fptr(scale_t, "scale_t"), _stream(stream)))
     return q, q_t, amax, scale, scale_t
 
 
 def fp8_scale_update(mode, amax=None, hist=None, pos=0, scale=None, scale_inv=None,
-                     clear_amax=False, stream=None):
+                     clear_amax=False, e5m2=False, stream=None):
     """One scale bookkeeping op on the device (see fp8lin.h for the modes).
-    ``clear_amax``: set amax to +0 after reading it (FROM_AMAX, RECORD)."""
+    ``clear_amax``: set amax to +0 after reading it (FROM_AMAX, RECORD).
+    ``e5m2``: scales for E5M2 codes (57344 in place of 448; FROM_AMAX, REFRESH)."""
     length = 0 if hist is None else hist.numel()
+    flags = (FP8_SCALE_CLEAR_AMAX if clear_amax else 0) | (FP8_E5M2 if e5m2 else 0)
     _check("fp8_scale_update", load().fp8_scale_update(
-        int(mode) | (FP8_SCALE_CLEAR_AMAX if clear_amax else 0), _fptr(amax, "amax"), _fptr(hist, "hist"), length, int(pos),
+        int(mode) | flags, _fptr(amax, "amax"), _fptr(hist, "hist"), length, int(pos),
         _fptr(scale, "scale"), _fptr(scale_inv, "scale_inv"), _stream(stream)))
 
 
 def fp8_linear_fwd(qx, qw, sx, sw, y=None, M_valid=None, gran=FP8_TENSORWISE, stream=None,
-                   bias=None):
-    """y [M, N] bf16 = sx * sw * qx [M, K] . qw [N, K]^T (+ bias [N], bf16, in the epilogue)."""
+                   bias=None, a_e5m2=False):
+    """y [M, N] bf16 = sx * sw * qx [M, K] . qw [N, K]^T (+ bias [N], bf16, in the epilogue).
+    ``a_e5m2``: qx holds E5M2 codes."""
+    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
     qx, qw = _codes(qx), _codes(qw)
     M, K = qx.shape
     N = qw.shape[0]
@@ -220,8 +227,10 @@ def fp8_bias_grad(g, rows_valid=None, db=None, stream=None):
     return db
 
 
-def fp8_linear_dgrad(qg, qw_t, sg, sw, dx=None, M_valid=None, gran=FP8_TENSORWISE, stream=None):
-    """dx [M, K] bf16 = sg * sw * qg [M, N] . qw_t [K, N]^T."""
+def fp8_linear_dgrad(qg, qw_t, sg, sw, dx=None, M_valid=None, gran=FP8_TENSORWISE, stream=None,
+                     a_e5m2=False):
+    """dx [M, K] bf16 = sg * sw * qg [M, N] . qw_t [K, N]^T. ``a_e5m2``: qg holds E5M2 codes."""
+    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
     qg, qw_t = _codes(qg), _codes(qw_t)
     M, N = qg.shape
     K = qw_t.shape[0]
@@ -236,8 +245,11 @@ def fp8_linear_dgrad(qg, qw_t, sg, sw, dx=None, M_valid=None, gran=FP8_TENSORWIS
     return dx
 
 
-def fp8_linear_wgrad(qg_t, qx_t, sg, sx, dw=None, gran=FP8_TENSORWISE, stream=None):
-    """dw [N, K] bf16 = sg * sx * qg_t [N, M] . qx_t [K, M]^T."""
+def fp8_linear_wgrad(qg_t, qx_t, sg, sx, dw=None, gran=FP8_TENSORWISE, stream=None,
+                     a_e5m2=False):
+    """dw [N, K] bf16 = sg * sx * qg_t [N, M] . qx_t [K, M]^T. ``a_e5m2``: qg_t holds E5M2
+    codes."""
+    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
     qg_t, qx_t = _codes(qg_t), _codes(qx_t)
     N, M = qg_t.shape
     K = qx_t.shape[0]

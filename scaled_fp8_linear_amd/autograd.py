@@ -116,8 +116,11 @@ class Fp8Linear(torch.nn.Module):
     """
 
     def __init__(self, in_features: int, out_features: int, bias: bool = False, device=None,
-                 update_interval: int = 16):
+                 update_interval: int = 16, grad_format: str = "e4m3"):
         super().__init__()
+        if grad_format not in ("e4m3", "e5m2"):
+            raise ValueError(f"grad_format must be 'e4m3' or 'e5m2', not {grad_format!r}")
+        self.grad_format = grad_format
         self.in_features, self.out_features = in_features, out_features
         self.weight = torch.nn.Parameter(
             torch.empty((out_features, in_features), dtype=torch.bfloat16, device=device))
@@ -141,7 +144,8 @@ class Fp8Linear(torch.nn.Module):
     def _begin(self) -> None:
         st = _state
         if self._lin is None or self._generation != st.generation:
-            self._lin = DelayedScalingLinear(self.weight.device, self.update_interval)
+            self._lin = DelayedScalingLinear(self.weight.device, self.update_interval,
+                                             grad_format=self.grad_format)
             self._generation, self._last_step, self._pending = st.generation, 0, False
         if self._last_step == st.step_count:
             return

@@ -40,7 +40,7 @@ constexpr int64_t kMaxContraction = (int64_t)1 << 17;
 // Checks shared by the three GEMM entry points. A is [rows_a, kc], B is [rows_b, kc].
 int check_gemm(const char* fn, const void* a, const void* b, const float* s1, const float* s2,
                const void* d, int64_t rows_a, int64_t rows_b, int64_t kc, int64_t m_valid,
-               int gran) {
+               int gran, bool a_e5m2) {
   if (rows_a < 0 || rows_b < 0 || kc < 0)
     return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
   if (rows_a % 16 || rows_b % 16 || kc % 16)
@@ -54,6 +54,8 @@ int check_gemm(const char* fn, const void* a, const void* b, const float* s1, co
   if (gran != FP8_TENSORWISE && gran != FP8_BLOCK_1x128)
     return fail(FP8_ERR_UNSUPPORTED, "%s: granularity %d (use FP8_TENSORWISE or FP8_BLOCK_1x128)",
                 fn, gran);
+  if (a_e5m2 && gran != FP8_TENSORWISE)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: e5m2 operands (FP8_A_E5M2) are for FP8_TENSORWISE", fn);
   if (gran == FP8_BLOCK_1x128 && kc % 128)
     return fail(FP8_ERR_SHAPE, "%s: block recipe needs the contraction size %% 128 == 0 (got %lld)",
                 fn, (long long)kc);
@@ -86,9 +88,12 @@ int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_va
                       float* scale_t, void* stream) {
   const char* fn = "fp8_quantize_amax";
   const bool accumulate = (gran & FP8_AMAX_ACCUMULATE) != 0;
-  gran &= ~FP8_AMAX_ACCUMULATE;
+  const bool e5m2 = (gran & FP8_E5M2) != 0;
+  gran &= ~(FP8_AMAX_ACCUMULATE | FP8_E5M2);
   if (accumulate && gran != FP8_TENSORWISE)
     return fail(FP8_ERR_UNSUPPORTED, "%s: FP8_AMAX_ACCUMULATE is for FP8_TENSORWISE", fn);
+  if (e5m2 && gran != FP8_TENSORWISE)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: FP8_E5M2 codes are for FP8_TENSORWISE", fn);
   if (rows < 0 || cols < 0) return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
   if (rows_valid < 0 || rows_valid > rows)
     return fail(FP8_ERR_SHAPE, "%s: rows_valid=%lld outside [0, %lld]", fn, (long long)rows_valid,
@@ -111,7 +116,7 @@ int fp8_quantize_amax(const void* x, int64_t rows, int64_t cols, int64_t rows_va
         return fail(FP8_ERR_UNSUPPORTED, "%s: scale/scale_t are outputs of the block modes only", fn);
       return hip_status(
           fp8lin::launch_quantize_tensorwise(xb, rows, cols, rows_valid, scale_inv, qb, qtb, amax,
-                                             accumulate, s),
+                                             accumulate, e5m2, s),
           fn);
     case FP8_BLOCK_1x128:
     case FP8_BLOCK_128x128:
@@ -140,9 +145,12 @@ int fp8_scale_update(int mode, float* amax, float* hist, int32_t len, int32_t po
                      float* scale, float* scale_inv, void* stream) {
   const char* fn = "fp8_scale_update";
   const bool clear = (mode & FP8_SCALE_CLEAR_AMAX) != 0;
-  mode &= ~FP8_SCALE_CLEAR_AMAX;
+  const bool e5m2 = (mode & FP8_E5M2) != 0;
+  mode &= ~(FP8_SCALE_CLEAR_AMAX | FP8_E5M2);
   if (clear && mode != FP8_SCALE_FROM_AMAX && mode != FP8_SCALE_RECORD)
     return fail(FP8_ERR_UNSUPPORTED, "%s: FP8_SCALE_CLEAR_AMAX needs a mode that reads amax", fn);
+  if (e5m2 && mode != FP8_SCALE_FROM_AMAX && mode != FP8_SCALE_REFRESH)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: FP8_E5M2 goes with a mode that writes scales", fn);
   switch (mode) {
     case FP8_SCALE_FROM_AMAX:
       if (!amax || !scale || !scale_inv) return fail(FP8_ERR_NULL, "%s: NULL pointer", fn);
@@ -160,20 +168,22 @@ int fp8_scale_update(int mode, float* amax, float* hist, int32_t len, int32_t po
       return fail(FP8_ERR_UNSUPPORTED, "%s: unknown mode %d", fn, mode);
   }
   return hip_status(fp8lin::launch_scale_update(mode, amax, clear, hist, len, pos, scale,
-                                                scale_inv, as_stream(stream)),
+                                                scale_inv, e5m2, as_stream(stream)),
                     fn);
 }
 
 int fp8_linear_fwd(const void* qx, const void* qw, const float* sx, const float* sw, void* y,
                    int64_t M, int64_t N, int64_t K, int64_t M_valid, int gran, void* stream) {
-  int e = check_gemm("fp8_linear_fwd", qx, qw, sx, sw, y, M, N, K, M_valid, gran);
+  const bool a5 = (gran & FP8_A_E5M2) != 0;
+  gran &= ~FP8_A_E5M2;
+  int e = check_gemm("fp8_linear_fwd", qx, qw, sx, sw, y, M, N, K, M_valid, gran, a5);
   if (e) return e;
   if (gran == FP8_BLOCK_1x128 && N % 128)
     return fail(FP8_ERR_SHAPE, "fp8_linear_fwd: block recipe needs N %% 128 == 0");
   return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qx),
                                             static_cast<const uint8_t*>(qw), sx, sw, nullptr,
                                             static_cast<uint16_t*>(y), M, N, K, M_valid,
-                                            gran == FP8_BLOCK_1x128, 128, as_stream(stream)),
+                                            gran == FP8_BLOCK_1x128, 128, a5, as_stream(stream)),
                     "fp8_linear_fwd");
 }
 
@@ -183,7 +193,9 @@ int fp8_linear_fwd_bias(const void* qx, const void* qw, const float* sx, const f
   const char* fn = "fp8_linear_fwd_bias";
   if (bias == nullptr)
     return fp8_linear_fwd(qx, qw, sx, sw, y, M, N, K, M_valid, gran, stream);
-  int e = check_gemm(fn, qx, qw, sx, sw, y, M, N, K, M_valid, gran);
+  if (gran & FP8_A_E5M2)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: the bias epilogue takes e4m3 operands", fn);
+  int e = check_gemm(fn, qx, qw, sx, sw, y, M, N, K, M_valid, gran, false);
   if (e) return e;
   if (gran != FP8_TENSORWISE)
     return fail(FP8_ERR_UNSUPPORTED, "%s: the bias epilogue is for FP8_TENSORWISE", fn);
@@ -192,7 +204,7 @@ int fp8_linear_fwd_bias(const void* qx, const void* qw, const float* sx, const f
                                             static_cast<const uint8_t*>(qw), sx, sw,
                                             static_cast<const uint16_t*>(bias),
                                             static_cast<uint16_t*>(y), M, N, K, M_valid, false,
-                                            128, as_stream(stream)),
+                                            128, false, as_stream(stream)),
                     fn);
 }
 
@@ -218,25 +230,29 @@ int fp8_bias_grad(const void* g, int64_t rows, int64_t cols, int64_t rows_valid,
 
 int fp8_linear_dgrad(const void* qg, const void* qw_t, const float* sg, const float* sw, void* dx,
                      int64_t M, int64_t N, int64_t K, int64_t M_valid, int gran, void* stream) {
-  int e = check_gemm("fp8_linear_dgrad", qg, qw_t, sg, sw, dx, M, K, N, M_valid, gran);
+  const bool a5 = (gran & FP8_A_E5M2) != 0;
+  gran &= ~FP8_A_E5M2;
+  int e = check_gemm("fp8_linear_dgrad", qg, qw_t, sg, sw, dx, M, K, N, M_valid, gran, a5);
   if (e) return e;
   if (gran == FP8_BLOCK_1x128 && K % 128)
     return fail(FP8_ERR_SHAPE, "fp8_linear_dgrad: block recipe needs K %% 128 == 0");
   return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qg),
                                             static_cast<const uint8_t*>(qw_t), sg, sw, nullptr,
                                             static_cast<uint16_t*>(dx), M, K, N, M_valid,
-                                            gran == FP8_BLOCK_1x128, 128, as_stream(stream)),
+                                            gran == FP8_BLOCK_1x128, 128, a5, as_stream(stream)),
                     "fp8_linear_dgrad");
 }
 
 int fp8_linear_wgrad(const void* qg_t, const void* qx_t, const float* sg, const float* sx, void* dw,
                      int64_t M, int64_t N, int64_t K, int gran, void* stream) {
-  int e = check_gemm("fp8_linear_wgrad", qg_t, qx_t, sg, sx, dw, N, K, M, N, gran);
+  const bool a5 = (gran & FP8_A_E5M2) != 0;
+  gran &= ~FP8_A_E5M2;
+  int e = check_gemm("fp8_linear_wgrad", qg_t, qx_t, sg, sx, dw, N, K, M, N, gran, a5);
   if (e) return e;
   return hip_status(fp8lin::launch_gemm_fp8(static_cast<const uint8_t*>(qg_t),
                                             static_cast<const uint8_t*>(qx_t), sg, sx, nullptr,
                                             static_cast<uint16_t*>(dw), N, K, M, N,
-                                            gran == FP8_BLOCK_1x128, 1, as_stream(stream)),
+                                            gran == FP8_BLOCK_1x128, 1, a5, as_stream(stream)),
                     "fp8_linear_wgrad");
 }
 

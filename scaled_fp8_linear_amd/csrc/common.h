@@ -8,6 +8,8 @@ namespace fp8lin {
 
 constexpr float kE4M3Max = 448.0f;     // largest finite OCP e4m3 value
 constexpr uint32_t kE4M3MaxBits = 0x43E00000u;   // 448.0f
+constexpr float kE5M2Max = 57344.0f;   // largest finite OCP e5m2 value (1.75 * 2^15)
+constexpr uint32_t kE5M2MaxBits = 0x47600000u;   // 57344.0f
 constexpr uint32_t kF32InfBits = 0x7F800000u;
 constexpr float kAmaxFloor = 1e-12f;   // lower clamp of amax before 448/amax
 
@@ -55,6 +57,23 @@ __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), lo, true);
 }
 
+// OCP e5m2 (sign, 5 exponent bits with bias 15, 2 mantissa bits; 0x7C is infinity,
+// 0x7D..0x7F NaN), used for gradients in the hybrid format. Saturation at +-57344
+// as for e4m3, so the converter never sees an out-of-range value.
+__device__ __forceinline__ float sat_e5m2(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t a = u & 0x7FFFFFFFu;
+  bool over = (a > kE5M2MaxBits) & (a <= kF32InfBits);
+  return over ? __uint_as_float((u & 0x80000000u) | kE5M2MaxBits) : v;
+}
+
+// Four floats -> four OCP e5m2 codes in one dword (a in the low byte); gfx950's
+// v_cvt_pk_bf8_f32 rounds to nearest even.
+__device__ __forceinline__ uint32_t cvt4_e5m2(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_bf8_f32(sat_e5m2(a), sat_e5m2(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(sat_e5m2(c), sat_e5m2(d), lo, true);
+}
+
 // Sign bits of four bf16 values (elements 0,1 in d0, 2,3 in d1) placed at
 // bit 7 of bytes 0..3.
 __device__ __forceinline__ uint32_t sign_bytes(uint32_t d0, uint32_t d1) {
@@ -74,12 +93,34 @@ __device__ __forceinline__ uint32_t fix_nan_codes(uint32_t codes, uint32_t signs
   return codes;
 }
 
+// e5m2: after saturation every finite code is at most 0x7B in magnitude, so a
+// magnitude of 0x7D..0x7F marks a NaN product, whatever NaN code the converter
+// picked; it becomes 0x7F with the sign of its input, as for e4m3.
+__device__ __forceinline__ uint32_t fix_nan_codes_e5m2(uint32_t codes, uint32_t signs) {
+  const uint32_t ff = ((codes & 0x7F7F7F7Fu) + 0x03030303u) & 0x80808080u;
+  if (__builtin_expect(ff != 0u, 0)) {
+    const uint32_t m = (ff >> 7) * 0xFFu;
+    codes = (codes & ~m) | (m & (0x7F7F7F7Fu | signs));
+  }
+  return codes;
+}
+
 // Four bf16 inputs (packed in d0, d1) times their multipliers -> four codes.
 __device__ __forceinline__ uint32_t quant4(uint32_t d0, uint32_t d1, float s0, float s1, float s2,
                                            float s3) {
   const uint32_t c = cvt4_e4m3(bf16_lo(d0) * s0, bf16_hi(d0) * s1, bf16_lo(d1) * s2,
                                bf16_hi(d1) * s3);
   return fix_nan_codes(c, sign_bytes(d0, d1));
+}
+
+// The same in a chosen format: FMT 0 e4m3, 1 e5m2.
+template <int FMT>
+__device__ __forceinline__ uint32_t quant4_fmt(uint32_t d0, uint32_t d1, float s0, float s1,
+                                               float s2, float s3) {
+  if constexpr (FMT == 0) return quant4(d0, d1, s0, s1, s2, s3);
+  const uint32_t c = cvt4_e5m2(bf16_lo(d0) * s0, bf16_hi(d0) * s1, bf16_lo(d1) * s2,
+                               bf16_hi(d1) * s3);
+  return fix_nan_codes_e5m2(c, sign_bytes(d0, d1));
 }
 
 // Two floats -> two bf16 in one dword (a in the low half), round to nearest even
@@ -100,10 +141,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // Scale pair from an amax: a = max(amax, 1e-12) keeping NaN, then two IEEE
 // divisions (this translation unit is built without fast-math, so '/' is the
 // correctly rounded float32 division).
-__device__ __forceinline__ void scale_pair(float amax, float* scale, float* scale_inv) {
+// fmax is the format's largest finite value (448 for e4m3, 57344 for e5m2).
+__device__ __forceinline__ void scale_pair(float amax, float* scale, float* scale_inv,
+                                           float fmax = kE4M3Max) {
   float a = (amax < kAmaxFloor) ? kAmaxFloor : amax;   // NaN < x is false: NaN kept
-  *scale = a / kE4M3Max;
-  *scale_inv = kE4M3Max / a;
+  *scale = a / fmax;
+  *scale_inv = fmax / a;
 }
 
 // Wavefront (64 lanes) max of an unsigned value.

@@ -149,10 +149,13 @@ __device__ __forceinline__ void wait_vm_lgkm() {
 }
 
 // Tile configuration. BROWS: 0 tensorwise, 1 or 128 block recipe (rows per B scale).
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int SWZ_, int GROUP_M_, int BROWS_>
+// AFMT: format of the A codes as the f8f6f4 MFMAs number it (0 OCP e4m3, 1 OCP e5m2);
+// B is always e4m3. The block recipe takes e4m3 only.
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int SWZ_, int GROUP_M_, int BROWS_,
+          int AFMT_ = 0>
 struct PCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_, SWZ = SWZ_;
-  static constexpr int GROUP_M = GROUP_M_, BROWS = BROWS_;
+  static constexpr int GROUP_M = GROUP_M_, BROWS = BROWS_, AFMT = AFMT_;
   static constexpr bool BLOCK = BROWS_ != 0;
   static constexpr int kWaves = WM * WN, kThreads = kWaves * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
@@ -163,6 +166,7 @@ struct PCfg {
   static_assert(STAGES >= 2 && STAGES <= 5, "stages");
   static_assert(!BLOCK || (STAGES % 2 == 0 && (BROWS == 1 || BN % 128 == 0)), "block recipe");
   static_assert(!BLOCK || BROWS == 1 || WTN <= 128, "one weight scale row per wave");
+  static_assert(!BLOCK || AFMT == 0, "block recipe: e4m3 operands");
 };
 
 // 64-byte rows: chunk c (0..3) of row r sits at c ^ f(r).
@@ -320,8 +324,8 @@ struct Tile {
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         if constexpr (!C::BLOCK) {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a, acc[i][j], 0, 0, 0,
-                                                                      0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a, acc[i][j], 0,
+                                                                      C::AFMT, 0, 0, 0, 0);
         } else if constexpr (!ODD) {
           const v16f z = {};
           part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a, z, 0, 0, 0, 0,
@@ -660,8 +664,8 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 #pragma unroll
       for (int j = 0; j < CT; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Alo[i],
-                                                                     FIRST ? z : acc[i][j], 0, 0,
-                                                                     0, 0, 0, 0);
+                                                                     FIRST ? z : acc[i][j], 0,
+                                                                     C::AFMT, 0, 0, 0, 0);
 #pragma unroll
     for (int x = 0; x < RH * CT; ++x) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -684,8 +688,8 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     for (int x = 0; x < kSecond; ++x) {
       const int i = RH + x / CT, j = x % CT;
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Ahi[i - RH],
-                                                                   FIRST ? z : acc[i][j], 0, 0, 0,
-                                                                   0, 0, 0);
+                                                                   FIRST ? z : acc[i][j], 0,
+                                                                   C::AFMT, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (x * kDma / kSecond != (x + 1) * kDma / kSecond) dma(x * kDma / kSecond, mine, r, kb);
       if (!LAST && x * kReads / kSecond != (x + 1) * kReads / kSecond) {
@@ -1283,15 +1287,15 @@ hipError_t run_persist(const uint8_t* A, const uint8_t* B, const float* sa, cons
 // Tensorwise: 256x256 tiles, 8 waves of 128x64 (four 32 KiB stages) for large problems;
 // 128x128 tiles, 4 waves of 64x64 for small ones. Two-stage variants take step counts
 // that are even but not multiples of four.
-using TwBig = PCfg<256, 256, 2, 4, 4, 0, 8, 0>;
-using TwBig2 = PCfg<256, 256, 2, 4, 2, 0, 8, 0>;
-using TwSmall = PCfg<128, 128, 2, 2, 4, 0, 8, 0>;
-using TwSmall2 = PCfg<128, 128, 2, 2, 2, 0, 8, 0>;
+template <int AF> using TwBig = PCfg<256, 256, 2, 4, 4, 0, 8, 0, AF>;
+template <int AF> using TwBig2 = PCfg<256, 256, 2, 4, 2, 0, 8, 0, AF>;
+template <int AF> using TwSmall = PCfg<128, 128, 2, 2, 4, 0, 8, 0, AF>;
+template <int AF> using TwSmall2 = PCfg<128, 128, 2, 2, 2, 0, 8, 0, AF>;
 // 16x16x128 kernel: 256x256 tiles, 4 waves of 128x128 (its own LDS plan); 224-row or
 // 224-column tiles where they split the output into whole rounds of 256 tiles better.
-using TwMx16 = PCfg<256, 256, 2, 2, 2, 0, 8, 0>;
-using TwMx16M224 = PCfg<224, 256, 2, 2, 2, 0, 8, 0>;
-using TwMx16N224 = PCfg<256, 224, 2, 2, 2, 0, 8, 0>;
+template <int AF> using TwMx16 = PCfg<256, 256, 2, 2, 2, 0, 8, 0, AF>;
+template <int AF> using TwMx16M224 = PCfg<224, 256, 2, 2, 2, 0, 8, 0, AF>;
+template <int AF> using TwMx16N224 = PCfg<256, 224, 2, 2, 2, 0, 8, 0, AF>;
 // Block recipe: the partial sums need a second set of accumulators, so 256x128 tiles.
 // With one weight scale per 128 rows, 8 waves of 64x64; with a B scale per row (wgrad),
 // 8 waves of 128x32, so that a lane needs 16 B scales per 128-wide K block, not 32.
@@ -1327,6 +1331,8 @@ hipError_t run_mx16(const uint8_t* A, const uint8_t* B, const float* sa, const f
   else if (bias == nullptr)
     hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, true, false>), g, b, 0, s, A, B, sa, sb, bias, D,
                        M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  else if constexpr (C::AFMT != 0)
+    return hipErrorInvalidValue;   // the host never asks for a bias with e5m2 codes
   else if (!tail)
     hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, false, true>), g, b, 0, s, A, B, sa, sb, bias, D,
                        M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
@@ -1394,30 +1400,17 @@ hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const 
   return run_persist<Blk2<BROWS>>(A, B, sa, sb, nullptr, D, M, N, K, M_valid, s);
 }
 
-}  // namespace
-
-hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
-                           const uint16_t* bias, uint16_t* D, int64_t M, int64_t N, int64_t K,
-                           int64_t M_valid, bool block_scaled, int b_rows_per_scale,
-                           hipStream_t s) {
-  if (M == 0 || N == 0) return hipSuccess;
-  // an empty contraction (e.g. a weight gradient over no tokens): every sum is +0, so the
-  // valid rows hold the bias (if any)
-  if (K == 0) {
-    if (bias != nullptr) return launch_bias_rows(bias, D, M, N, M_valid, s);
-    return launch_fill_u32(reinterpret_cast<uint32_t*>(D), 0u, M * N / 2, s);
-  }
-  const int m = (int)M, n = (int)N, k = (int)K, mv = (int)M_valid;
-  if (block_scaled) {
-    if (b_rows_per_scale == 1) return run_block<1>(A, B, sa, sb, D, m, n, k, mv, s);
-    return run_block<128>(A, B, sa, sb, D, m, n, k, mv, s);
-  }
-  // tensorwise: the 16x16x128 kernel for K of at least 512 when the output spans at least
-  // 64 of its tiles; else the 32x32x64 persistent kernel with 256x256 tiles, or 128x128
-  // tiles for small outputs.
-  // FP8LIN_GEMM_CFG (0: 256x256, 1: 128x128, 2: 16x16x128) forces a choice for sweeps.
+// Tensorwise dispatch for one A format.
+// The 16x16x128 kernel for K of at least 512 when the output spans at least 64 of its
+// tiles; else the 32x32x64 persistent kernel with 256x256 tiles, or 128x128 tiles for
+// small outputs. FP8LIN_GEMM_CFG (0: 256x256, 1: 128x128, 2: 16x16x128) forces a choice
+// for sweeps.
+template <int AF>
+hipError_t run_tensorwise_fmt(const uint8_t* A, const uint8_t* B, const float* sa,
+                              const float* sb, const uint16_t* bias, uint16_t* D, int m, int n,
+                              int k, int mv, hipStream_t s) {
   const bool mx16_ok = k >= 4 * kStageK;
-  const bool big = (int64_t)M * N >= (int64_t)2048 * 2048;
+  const bool big = (int64_t)m * n >= (int64_t)2048 * 2048;
   int cfg = forced_cfg();
   if (cfg < 0) cfg = big ? (mx16_ok ? 2 : 0) : 1;
   if (cfg == 2 && mx16_ok) {
@@ -1431,13 +1424,40 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, 
     const int64_t c0 = cost(256, 256), cm = cost(224, 256), cn = cost(256, 224);
     if (c0 > 256 * 256) {
       if (cm < c0 && cm <= cn)
-        return run_mx16<TwMx16M224>(A, B, sa, sb, bias, D, m, n, k, mv, s);
-      if (cn < c0) return run_mx16<TwMx16N224>(A, B, sa, sb, bias, D, m, n, k, mv, s);
+        return run_mx16<TwMx16M224<AF>>(A, B, sa, sb, bias, D, m, n, k, mv, s);
+      if (cn < c0) return run_mx16<TwMx16N224<AF>>(A, B, sa, sb, bias, D, m, n, k, mv, s);
     }
-    return run_mx16<TwMx16>(A, B, sa, sb, bias, D, m, n, k, mv, s);
+    return run_mx16<TwMx16<AF>>(A, B, sa, sb, bias, D, m, n, k, mv, s);
   }
-  if (cfg == 1) return run_tensorwise<TwSmall, TwSmall2>(A, B, sa, sb, bias, D, m, n, k, mv, s);
-  return run_tensorwise<TwBig, TwBig2>(A, B, sa, sb, bias, D, m, n, k, mv, s);
+  if (cfg == 1)
+    return run_tensorwise<TwSmall<AF>, TwSmall2<AF>>(A, B, sa, sb, bias, D, m, n, k, mv, s);
+  return run_tensorwise<TwBig<AF>, TwBig2<AF>>(A, B, sa, sb, bias, D, m, n, k, mv, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
+                           const uint16_t* bias, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                           int64_t M_valid, bool block_scaled, int b_rows_per_scale, bool a_e5m2,
+                           hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  // an empty contraction (e.g. a weight gradient over no tokens): every sum is +0, so the
+  // valid rows hold the bias (if any)
+  if (K == 0) {
+    if (bias != nullptr) return launch_bias_rows(bias, D, M, N, M_valid, s);
+    return launch_fill_u32(reinterpret_cast<uint32_t*>(D), 0u, M * N / 2, s);
+  }
+  const int m = (int)M, n = (int)N, k = (int)K, mv = (int)M_valid;
+  if (block_scaled) {
+    if (a_e5m2) return hipErrorInvalidValue;
+    if (b_rows_per_scale == 1) return run_block<1>(A, B, sa, sb, D, m, n, k, mv, s);
+    return run_block<128>(A, B, sa, sb, D, m, n, k, mv, s);
+  }
+  if (a_e5m2) {
+    if (bias != nullptr) return hipErrorInvalidValue;
+    return run_tensorwise_fmt<1>(A, B, sa, sb, nullptr, D, m, n, k, mv, s);
+  }
+  return run_tensorwise_fmt<0>(A, B, sa, sb, bias, D, m, n, k, mv, s);
 }
 
 }  // namespace fp8lin

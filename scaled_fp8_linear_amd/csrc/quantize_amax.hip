@@ -1,10 +1,12 @@
-// Fused bf16 -> e4m3 quantize + amax + transposed copy (tensorwise scaling).
+// Fused bf16 -> e4m3 (or e5m2) quantize + amax + transposed copy (tensorwise scaling).
 //
 // What it computes (AstrAI, astrai/extension/fp8_state.py: module comment on
 // the GEMM layout and fp8_linear_forward's docstring): for a bf16 [rows, cols]
 // tensor x and the float32 multiplier scale_inv (= 448/amax of the scale in
 // force), q[r,c] = e4m3(float32(x[r,c]) * scale_inv), its transpose q_t, and
 // amax = max|x| over the valid rows, taken in the same pass ("free" amax).
+// Gradients may instead be coded in OCP e5m2 (the hybrid format: wider range,
+// one mantissa bit less), with the multiplier 57344/amax.
 //
 // Design (HBM-bound: 2 bytes read, 2 bytes written per element):
 //  * a workgroup of 256 lanes owns a TR x TC tile (128 x 256);
@@ -67,7 +69,8 @@ __device__ __forceinline__ void st8(void* p, uint32_t a, uint32_t b) {
   else *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
 }
 
-template <class QC>
+// FMT: 0 OCP e4m3 codes, 1 OCP e5m2 codes (gradients in the hybrid format).
+template <class QC, int FMT>
 __global__ void __launch_bounds__(QC::kQThreads)
 quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                            int64_t rows_valid, const float* __restrict__ scale_inv_p,
@@ -131,8 +134,8 @@ quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t
       uint32_t lo[4], hi[4];   // codes of columns 0..3 / 4..7 of each row
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lo[i] = quant4(v[p][i].x, v[p][i].y, s, s, s, s);
-        hi[i] = quant4(v[p][i].z, v[p][i].w, s, s, s, s);
+        lo[i] = quant4_fmt<FMT>(v[p][i].x, v[p][i].y, s, s, s, s);
+        hi[i] = quant4_fmt<FMT>(v[p][i].z, v[p][i].w, s, s, s, s);
         if (!ok[p][i]) { lo[i] = 0u; hi[i] = 0u; }      // padding rows are written as 0x00
       }
       if (want_q) {
@@ -209,14 +212,20 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
 
 template <class QC>
 hipError_t run_q(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_valid,
-                 const float* scale_inv, uint8_t* q, uint8_t* q_t, float* amax, hipStream_t s) {
+                 const float* scale_inv, uint8_t* q, uint8_t* q_t, float* amax, bool e5m2,
+                 hipStream_t s) {
   const int64_t tiles_r = (rows + QC::kQTR - 1) / QC::kQTR;
   const int64_t tiles_c = (cols + QC::kQTC - 1) / QC::kQTC;
   const int64_t tiles = tiles_r * tiles_c;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quantize_tensorwise_kernel<QC>, dim3((unsigned)tiles), dim3(QC::kQThreads), 0,
-                     s, x, rows, cols, rows_valid, scale_inv, q, q_t,
-                     reinterpret_cast<uint32_t*>(amax), tiles_c);
+  if (e5m2)
+    hipLaunchKernelGGL((quantize_tensorwise_kernel<QC, 1>), dim3((unsigned)tiles),
+                       dim3(QC::kQThreads), 0, s, x, rows, cols, rows_valid, scale_inv, q, q_t,
+                       reinterpret_cast<uint32_t*>(amax), tiles_c);
+  else
+    hipLaunchKernelGGL((quantize_tensorwise_kernel<QC, 0>), dim3((unsigned)tiles),
+                       dim3(QC::kQThreads), 0, s, x, rows, cols, rows_valid, scale_inv, q, q_t,
+                       reinterpret_cast<uint32_t*>(amax), tiles_c);
   return hipGetLastError();
 }
 
@@ -240,7 +249,8 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 
 hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t rows, int64_t cols,
                                       int64_t rows_valid, const float* scale_inv, uint8_t* q,
-                                      uint8_t* q_t, float* amax, bool accumulate, hipStream_t s) {
+                                      uint8_t* q_t, float* amax, bool accumulate, bool e5m2,
+                                      hipStream_t s) {
   hipError_t e = hipSuccess;
   if (amax != nullptr && !accumulate) {
     e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 0u, 1, s);
@@ -264,12 +274,12 @@ hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t rows, int64_t c
   // HBM alone, which costs a third of the rate on tall tensors (54672 x 4096: 3.4
   // against 4.7 TB/s), while the cached path merges neighbouring pieces first.
   switch (quant_cfg()) {
-    case 1: return run_q<QCfg<128, 256, 256, 7>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 2: return run_q<QCfg<128, 256, 256, 0>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 3: return run_q<QCfg<256, 256, 512, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 4: return run_q<QCfg<128, 512, 512, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    case 5: return run_q<QCfg<128, 256, 256, 2>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
-    default: return run_q<QCfg<128, 256, 256, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, s);
+    case 1: return run_q<QCfg<128, 256, 256, 7>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
+    case 2: return run_q<QCfg<128, 256, 256, 0>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
+    case 3: return run_q<QCfg<256, 256, 512, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
+    case 4: return run_q<QCfg<128, 512, 512, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
+    case 5: return run_q<QCfg<128, 256, 256, 2>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
+    default: return run_q<QCfg<128, 256, 256, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
   }
 }
 

@@ -7,7 +7,8 @@
 //  * FP8TensorMeta.refresh: m = max(hist); if m > 0: scale = m/448,
 //    scale_inv = 448/m.
 // Each quotient is one correctly rounded float32 division (no fast-math in
-// this translation unit, so '/' lowers to the IEEE division sequence).
+// this translation unit, so '/' lowers to the IEEE division sequence). For
+// gradients kept in e5m2 the format maximum 57344 takes the place of 448.
 #include "common.h"
 #include "launch.h"
 
@@ -17,10 +18,10 @@ namespace {
 
 // clear: amax[0] = +0 once read (the next quantize pass folds its max into it)
 __global__ void scale_from_amax_kernel(float* __restrict__ amax, float* __restrict__ scale,
-                                       float* __restrict__ scale_inv, int clear) {
+                                       float* __restrict__ scale_inv, int clear, float fmax) {
   const float a = amax[0];
   float s, si;
-  scale_pair(a, &s, &si);
+  scale_pair(a, &s, &si, fmax);
   scale[0] = s;
   scale_inv[0] = si;
   if (clear) amax[0] = 0.0f;
@@ -34,7 +35,7 @@ __global__ void record_kernel(float* __restrict__ amax, float* __restrict__ hist
 
 // One wavefront; len is small (16 for the pages' schedule).
 __global__ void refresh_kernel(const float* __restrict__ hist, int len, float* __restrict__ scale,
-                               float* __restrict__ scale_inv) {
+                               float* __restrict__ scale_inv, float fmax) {
   const int lane = threadIdx.x;
   // max with NaN propagation, as torch.max does: track NaN separately
   float m = 0.0f;
@@ -50,19 +51,21 @@ __global__ void refresh_kernel(const float* __restrict__ hist, int len, float* _
   for (int off = 32; off > 0; off >>= 1) r = fmaxf(r, __shfl_xor(r, off, 64));
   int anynan = __any(nan);
   if (lane == 0 && !anynan && r > 0.0f) {
-    scale[0] = r / kE4M3Max;
-    scale_inv[0] = kE4M3Max / r;
+    scale[0] = r / fmax;
+    scale_inv[0] = fmax / r;
   }
 }
 
 }  // namespace
 
 hipError_t launch_scale_update(int mode, float* amax, bool clear_amax, float* hist, int32_t len,
-                               int32_t pos, float* scale, float* scale_inv, hipStream_t s) {
+                               int32_t pos, float* scale, float* scale_inv, bool e5m2,
+                               hipStream_t s) {
+  const float fmax = e5m2 ? kE5M2Max : kE4M3Max;
   switch (mode) {
     case 0:
       hipLaunchKernelGGL(scale_from_amax_kernel, dim3(1), dim3(1), 0, s, amax, scale, scale_inv,
-                         (int)clear_amax);
+                         (int)clear_amax, fmax);
       break;
     case 1:
       hipLaunchKernelGGL(record_kernel, dim3(1), dim3(1), 0, s, amax, hist, (int)pos,
@@ -70,7 +73,7 @@ hipError_t launch_scale_update(int mode, float* amax, bool clear_amax, float* hi
       break;
     case 2:
       hipLaunchKernelGGL(refresh_kernel, dim3(1), dim3(64), 0, s, (const float*)hist, (int)len,
-                         scale, scale_inv);
+                         scale, scale_inv, fmax);
       break;
     default:
       return hipErrorInvalidValue;

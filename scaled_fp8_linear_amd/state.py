@@ -11,7 +11,8 @@ and step counter, and the order of calls:
                    delayed x scale, forward GEMM, FROM_AMAX(amax_x) -> next slot
     backward(g)    quantize g with the delayed g scale, dgrad (Qg, Qw^T),
                    wgrad (Qg^T, Qx^T with the scale that made Qx^T),
-                   FROM_AMAX(amax_g) -> next slot
+                   FROM_AMAX(amax_g) -> next slot (g in E4M3, or in E5M2 for
+                   the hybrid format)
     end_step()     the next slots become current
 
 Reading: the activation and gradient scales live in two slots (current,
@@ -48,10 +49,16 @@ class DelayedScalingLinear:
     and "scale".
     """
 
-    def __init__(self, device, update_interval: int = 16, probe=None, keep_amax: bool = False):
+    def __init__(self, device, update_interval: int = 16, probe=None, keep_amax: bool = False,
+                 grad_format: str = "e4m3"):
         """``keep_amax``: leave each amax in its buffer after the update that reads it (every
         quantize pass then zeroes its buffer first: one more launch per pass); for
-        inspecting the amaxes of a step."""
+        inspecting the amaxes of a step. ``grad_format`` "e5m2": the hybrid format, with the
+        output gradient coded in E5M2 (scales from 57344) and x, W in E4M3."""
+        if grad_format not in ("e4m3", "e5m2"):
+            raise ValueError(f"grad_format must be 'e4m3' or 'e5m2', not {grad_format!r}")
+        self.grad_format = grad_format
+        self._g5 = grad_format == "e5m2"
         self.probe = probe or _NoProbe()
         self.acc = not keep_amax
         f32 = dict(dtype=torch.float32, device=device)
@@ -125,21 +132,22 @@ class DelayedScalingLinear:
         p = self.probe
         qx_t, qw_t, rows_valid = self._saved
         sg, sg_inv = Slot(self.g_scale, self.cur), Slot(self.g_scale_inv, self.cur)
+        g5 = self._g5
         with p("quantize"):
             qg, qg_t, _, _, _ = _abi.fp8_quantize_amax(
                 g, rows_valid=rows_valid, scale_inv=sg_inv, q=b.get("qg"), q_t=b.get("qg_t"),
-                amax=self.amax_g, amax_accumulate=self.acc, stream=stream)
+                amax=self.amax_g, amax_accumulate=self.acc, e5m2=g5, stream=stream)
         with p("gemm"):
             dx = _abi.fp8_linear_dgrad(qg, qw_t, sg, self.w_scale, dx=dx, M_valid=rows_valid,
-                                       stream=stream)
+                                       stream=stream, a_e5m2=g5)
         with p("gemm"):
             dw = _abi.fp8_linear_wgrad(qg_t, qx_t, sg, Slot(self.x_scale, self.cur), dw=dw,
-                                       stream=stream)
+                                       stream=stream, a_e5m2=g5)
         with p("scale"):
             _abi.fp8_scale_update(_abi.FP8_SCALE_FROM_AMAX, amax=self.amax_g,
                                   scale=Slot(self.g_scale, self.nxt),
                                   scale_inv=Slot(self.g_scale_inv, self.nxt), clear_amax=self.acc,
-                                  stream=stream)
+                                  e5m2=g5, stream=stream)
         return dx, dw
 
     def end_step(self, g_updated: bool = True) -> None:
@@ -157,12 +165,14 @@ class DelayedScalingLinear:
         """The whole schedule state: device tensors cloned, host counters as ints."""
         d = {k: getattr(self, k).detach().clone() for k in self._TENSORS}
         d.update(step_count=self.step_count, idx=self.idx, cur=self.cur,
-                 update_interval=self.update_interval)
+                 update_interval=self.update_interval, grad_format=self.grad_format)
         return d
 
     def load_state_dict(self, d: dict) -> None:
         if int(d["update_interval"]) != self.update_interval:
             raise ValueError("update_interval differs from the saved state's")
+        if d.get("grad_format", "e4m3") != self.grad_format:
+            raise ValueError("grad_format differs from the saved state's")
         for k in self._TENSORS:
             getattr(self, k).copy_(d[k])
         self.step_count, self.idx, self.cur = int(d["step_count"]), int(d["idx"]), int(d["cur"])

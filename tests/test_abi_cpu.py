@@ -104,3 +104,17 @@ def test_amax_flag_checks(lib):
     # clear needs a mode that reads amax
     assert lib.fp8_scale_update(2 | 0x100, p, p, 16, 0, p, p, None) == 4
     assert lib.fp8_scale_update(0 | 0x100, None, None, 0, 0, p, p, None) == 1
+
+
+def test_e5m2_flag_checks(lib):
+    p = ctypes.c_void_p(16)
+    # E5M2 codes: tensorwise passes only
+    assert lib.fp8_quantize_amax(p, 128, 128, 128, 1 | 0x200, None, p, None, p, p, None,
+                                 None) == 4
+    # the format maximum matters only to modes that write scales
+    assert lib.fp8_scale_update(1 | 0x200, p, p, 16, 0, None, None, None) == 4
+    # an E5M2 first operand: tensorwise GEMMs only, and no bias epilogue
+    assert lib.fp8_linear_dgrad(p, p, p, p, p, 128, 128, 128, 128, 1 | 0x200, None) == 4
+    assert lib.fp8_linear_fwd_bias(p, p, p, p, p, p, 16, 16, 16, 16, 0x200, None) == 4
+    # the flag passes the host checks (shape errors are still reported as such)
+    assert lib.fp8_linear_wgrad(p, p, p, p, p, 24, 16, 16, 0x200, None) == 2
