@@ -473,33 +473,33 @@ def main():
     wts = {"gate": t["w_gate"], "up": t["w_up"], "down": t["w_down"]}
     grads = {"gate": t["g_gate"], "up": t["g_up"], "down": t["g_down"]}
 
-    def step():
+    def step(layers=lins):
         # token-count padding check (8192 is a multiple of 16: nothing to add)
         _, T_pad = m.fp8_pad_tokens(t["x"], query_only=True)
         assert T_pad == M
         for n in ("gate", "up", "down"):
-            lins[n].begin_step()
+            layers[n].begin_step()
         for n in ("gate", "up", "down"):
-            lins[n].forward(inp[n], wts[n], out=outs[n]["y"], bufs=bufs[n])
+            layers[n].forward(inp[n], wts[n], out=outs[n]["y"], bufs=bufs[n])
         for n in ("down", "up", "gate"):
-            lins[n].backward(grads[n], dx=outs[n]["dx"], dw=outs[n]["dw"], bufs=bufs[n])
+            layers[n].backward(grads[n], dx=outs[n]["dx"], dw=outs[n]["dw"], bufs=bufs[n])
         for n in ("gate", "up", "down"):
-            lins[n].end_step()
+            layers[n].end_step()
 
     for _ in range(args.warmup):
         step()
 
-    def timed_steps():
+    def timed_steps(layers=lins, steps=args.steps):
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record()
-        for _ in range(args.steps):
-            step()
+        for _ in range(steps):
+            step(layers)
         stop.record()
         torch.cuda.synchronize()
-        return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+        return start.elapsed_time(stop) / steps, time.perf_counter() - t0
 
     # the timed region: K steps with nothing recorded between the kernels
     ms_step, wall_s = timed_steps()
@@ -566,6 +566,31 @@ def main():
         "wall_s_timed": round(wall_s, 3),
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.headline_only:
+        # the hybrid format on the same inputs and buffers: gradients in E5M2
+        hprobe = EventProbe(torch)
+        hyb = {n: m.DelayedScalingLinear(dev, probe=hprobe, grad_format="e5m2")
+               for n in ("gate", "up", "down")}
+        hsteps = max(3, args.steps // 3)
+        for _ in range(2):
+            step(hyb)
+        ms_h, _ = timed_steps(hyb, hsteps)
+        hprobe.active = True
+        timed_steps(hyb, hsteps)
+        hprobe.active = False
+        h_gemm = hprobe.durations_ms("gemm")
+        # per step: 3 forward GEMMs (E4M3 x E4M3), then dgrad and wgrad of each linear
+        bwd = [d for i, d in enumerate(h_gemm) if i % 9 >= 3]
+        line["hybrid_e5m2_gradients"] = {
+            "workload": "the same MLP block with the output gradients coded in E5M2 "
+                        "(x, W in E4M3; dgrad/wgrad on the mixed-format MFMA)",
+            "tflops": round(flops_step / (ms_h * 1e-3) / 1e12, 2),
+            "ms_per_step": round(ms_h, 4),
+            "gemm_tflops_per_launch": round(gemm_flops / (float(np.mean(h_gemm)) * 1e-3) / 1e12, 2),
+            "backward_gemm_tflops_per_launch": round(
+                gemm_flops / (float(np.mean(bwd)) * 1e-3) / 1e12, 2),
+        }
+        del hyb
     del t, bufs, outs, lins
     if not args.headline_only:
         torch.cuda.empty_cache()
