@@ -195,3 +195,52 @@ def test_mixed_format_error_bound_uses_e5m2_norms():
     qb = np.array([[0x38, 0x38]], np.uint8)        # E4M3: 1, 1
     b = gemm.error_bound(qa, qb, 1.0, 1.0, a_fmt="e5m2")
     assert b[0, 0] == pytest.approx(1e-2 * np.sqrt(5.0) * np.sqrt(2.0), rel=1e-15)
+
+
+def test_bshd_alignment_worked_case(golden_dir):
+    """The review thread's case: B = 16, tp = 4 with TE's multiple 8. Padding T to
+    8 * tp / gcd(B, 8 * tp) gives a multiple of 2, which tp = 4 does not divide; the lcm
+    rule asks for 4."""
+    c = _golden_constants(golden_dir)
+    B, tp, base = int(c["bshd_example_batch"]), int(c["bshd_example_tp"]), int(c["bshd_te_base"])
+    naive = base * tp // np.gcd(B, base * tp)
+    assert naive == int(c["bshd_example_naive"]) == 2 and naive % tp != 0
+    assert padding.align_multiples(padding.BSHD, B, tp, base=base) == (4, 1)
+
+
+@pytest.mark.parametrize("B,tp,base", [(16, 4, 8), (16, 4, 16), (3, 2, 16), (1, 8, 16),
+                                       (6, 4, 16), (5, 3, 8), (32, 1, 16)])
+def test_bshd_alignment_is_the_least_valid_multiple(B, tp, base):
+    """Brute force: T is valid iff T % tp == 0 and B * T % (base * tp) == 0; the valid T
+    are exactly the multiples of the returned multiple."""
+    m, total = padding.align_multiples(padding.BSHD, B, tp, base=base)
+    assert total == 1
+    for T in range(1, 4 * m * base + 1):
+        valid = T % tp == 0 and (B * T) % (base * tp) == 0
+        assert valid == (T % m == 0), (B, tp, base, T)
+
+
+def test_thd_alignment(golden_dir):
+    c = _golden_constants(golden_dir)
+    assert c["thd_multiple_te"] == "8*cp*tp"
+    assert padding.align_multiples(padding.THD, tp=2, cp=1, base=8) == (1, 16)
+    assert padding.align_multiples(padding.THD, tp=2, cp=4) == (8, 128)
+    assert padding.align_multiples(padding.THD) == (1, 16)
+    with pytest.raises(ValueError):
+        padding.align_multiples(padding.BSHD, 4, 2, cp=2)
+
+
+def test_pad_and_unpad_varlen_by_hand():
+    x = (np.arange(7 * 2, dtype=np.uint16).reshape(7, 2) + 1)       # lengths 3, 1, 3
+    p, cu = padding.pad_varlen(x, [3, 1, 3], seq_multiple=4, total_multiple=16)
+    assert list(cu) == [0, 4, 8, 12] and p.shape == (16, 2)
+    assert np.array_equal(p[0:3], x[0:3]) and np.all(p[3] == 0)
+    assert np.array_equal(p[4], x[3]) and np.all(p[5:8] == 0)
+    assert np.array_equal(p[8:11], x[4:7]) and np.all(p[11:] == 0)
+    assert np.array_equal(padding.unpad_varlen(p, [3, 1, 3], cu), x)
+    # every sequence length a multiple already, no total padding: the identity
+    q, cu2 = padding.pad_varlen(x[:4], [2, 2], 2, 1)
+    assert np.array_equal(q, x[:4]) and list(cu2) == [0, 2, 4]
+    # empty sequences take no rows
+    r, cu3 = padding.pad_varlen(x[:3], [0, 3, 0], 4, 1)
+    assert list(cu3) == [0, 0, 4, 4] and r.shape == (4, 2)
