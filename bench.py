@@ -361,10 +361,45 @@ def measure_varlen(torch, m, workloads, steps, warmup):
     ms = _time_steps(torch, step_in_place, steps, warmup)
     ms_copy = _time_steps(torch, step_copy, steps, warmup)
     flops = 6.0 * T_pad * 4096 * 4096
+
+    # per-sequence alignment for tp = cp = 2 (THD): every sequence to a multiple of 4, the
+    # batch to a multiple of 64; pad and unpad timed per launch with HIP events
+    sm, tm = m.fp8_align_multiple(m.FP8_LAYOUT_THD, 1, 2, 2)
+    lens = workloads.varlen_lengths(4)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    _, cu_pad, T_al = m.fp8_pad_varlen(x, cu, sm, tm, query_only=True)
+    xa = torch.empty((T_al, x.shape[1]), dtype=x.dtype, device=dev)
+    xu = torch.empty_like(x)
+
+    def per_launch_ms(fn, n=20):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    pad_ms = per_launch_ms(lambda: m.fp8_pad_varlen(x, cu, sm, tm, x_pad=xa))
+    unpad_ms = per_launch_ms(lambda: m.fp8_unpad_varlen(xa, cu, cu_pad, x=xu))
+    cols = x.shape[1]
+    pad_bytes = 2 * T * cols + 2 * T_al * cols
+    unpad_bytes = 4 * T * cols
     return {"workload": "packed THD batch, 64 seqs U{32..2048}, K=N=4096, delayed scaling",
             "tokens": T, "tokens_padded": T_pad, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "ms_per_step": round(ms, 4), "padding": "in place (tail rows of the batch zeroed)",
-            "ms_per_step_padding_by_copy": round(ms_copy, 4)}
+            "ms_per_step_padding_by_copy": round(ms_copy, 4),
+            "per_sequence_alignment": {
+                "rule": "THD, tp = cp = 2: each sequence to a multiple of %d, the batch to %d"
+                        % (sm, tm),
+                "tokens_aligned": T_al,
+                "pad_us": round(pad_ms * 1e3, 1),
+                "pad_gbs": round(pad_bytes / (pad_ms * 1e-3) / 1e9, 1),
+                "unpad_us": round(unpad_ms * 1e3, 1),
+                "unpad_gbs": round(unpad_bytes / (unpad_ms * 1e-3) / 1e9, 1)}}
 
 
 def measure_f1(torch, m, steps, warmup):

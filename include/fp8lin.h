@@ -294,6 +294,69 @@ int fp8_bias_grad(const void* g, int64_t rows, int64_t cols, int64_t rows_valid,
 int fp8_pad_tokens(const void* x, int64_t T, int64_t cols, int32_t multiple, void* x_pad,
                    int64_t* T_pad, void* stream);
 
+/* Layouts of fp8_align_multiple. */
+enum { FP8_LAYOUT_THD = 0, FP8_LAYOUT_BSHD = 1 };
+
+/*
+ * fp8_align_multiple -- the token multiples a layout needs under tensor (tp),
+ * sequence and context (cp) parallelism. Host-only integer arithmetic.
+ *
+ * Source: [NeMo] review thread on BSHD padding: with sequence parallelism the
+ * local GEMM sees M = B*T/tp tokens, so FP8 needs B*T % (base*tp) == 0 and
+ * T % tp == 0, which padding T to base*tp/gcd(B, base*tp) alone does not
+ * give (the thread's case B=16, tp=4 asks only for a multiple of 2); the
+ * THD helper pads the packed total to base * cp_size * tp_size.
+ *
+ *   layout  FP8_LAYOUT_THD (packed): *seq_multiple = 2*cp if cp > 1 else 1 (a
+ *           reading: load-balanced context parallelism cuts each sequence into
+ *           2*cp chunks), *total_multiple = base*cp*tp.
+ *           FP8_LAYOUT_BSHD (B sequences padded to one length T; cp must be 1):
+ *           *seq_multiple = lcm(tp, base*tp/gcd(B, base*tp)) for T,
+ *           *total_multiple = 1.
+ *   batch   B (BSHD; ignored for THD), tp, cp, base >= 1 (base: the FP8 multiple,
+ *           16 for this library's GEMMs).
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_UNSUPPORTED (unknown layout,
+ * BSHD with cp > 1).
+ */
+int fp8_align_multiple(int layout, int64_t batch, int32_t tp, int32_t cp, int32_t base,
+                       int32_t* seq_multiple, int32_t* total_multiple);
+
+/*
+ * fp8_pad_varlen -- pad every sequence of a packed batch, then the batch.
+ *
+ * Source: [NeMo] review thread (per-layout token multiples, above); [NeMo-packed]
+ * NeMo Speech PR 16194 summary: padding-free packed batches with CP/FSDP/FP8
+ * alignment.
+ *
+ *   x             bf16 [cu_seqlens[nseq], cols], the sequences packed in order.
+ *   cu_seqlens    HOST int64 [nseq + 1]: 0 = cu[0] <= cu[1] <= ... (sequence i is
+ *                 rows cu[i] .. cu[i+1]).
+ *   seq_multiple  each sequence of length L takes L + ((-L) mod seq_multiple) rows;
+ *   total_multiple  the padded sequences' end E is padded to E + ((-E) mod total_multiple).
+ *   cu_seqlens_pad  HOST int64 [nseq + 1] out (required with x_pad): where sequence i
+ *                 starts in x_pad; cu_seqlens_pad[nseq] = E.
+ *   T_pad         HOST int64 out, required: the padded row count.
+ *   x_pad         NULL: only the offsets are computed (nothing is enqueued).
+ *                 Otherwise bf16 [T_pad, cols], not aliasing x: sequence rows copied,
+ *                 every padding row zero.
+ *   cols          a multiple of 16; x and x_pad 16-byte aligned.
+ * Zero padding rows quantize to 0x00 and add nothing to any GEMM sum; the
+ * forward output and dx at those rows are 0 (without a bias).
+ */
+int fp8_pad_varlen(const void* x, const int64_t* cu_seqlens, int32_t nseq, int64_t cols,
+                   int32_t seq_multiple, int32_t total_multiple, void* x_pad,
+                   int64_t* cu_seqlens_pad, int64_t* T_pad, void* stream);
+
+/*
+ * fp8_unpad_varlen -- the inverse gather: x[cu[i] + j] = x_pad[cu_pad[i] + j] for
+ * j < cu[i+1] - cu[i] (e.g. dx of a padded batch back to the packed tokens).
+ *   x_pad bf16 [>= cu_pad[nseq], cols]; x bf16 [cu[nseq], cols], not aliasing x_pad.
+ *   cu_seqlens, cu_seqlens_pad  HOST int64 [nseq + 1], both from 0 and non-decreasing,
+ *   every padded sequence at least as long as its sequence.
+ */
+int fp8_unpad_varlen(const void* x_pad, const int64_t* cu_seqlens, const int64_t* cu_seqlens_pad,
+                     int32_t nseq, int64_t cols, void* x, void* stream);
+
 /* Message for the last error returned on the calling thread ("" if none). */
 const char* fp8_last_error(void);
 

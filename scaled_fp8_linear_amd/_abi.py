@@ -26,7 +26,9 @@ FP8_A_E5M2 = 0x200              # flag for the GEMMs: the first operand holds E5
 
 EXPORTS = ("fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
            "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version",
-           "fp8_linear_fwd_bias", "fp8_bias_grad")
+           "fp8_linear_fwd_bias", "fp8_bias_grad", "fp8_align_multiple", "fp8_pad_varlen",
+           "fp8_unpad_varlen")
+FP8_LAYOUT_THD, FP8_LAYOUT_BSHD = 0, 1
 
 
 class Fp8Error(RuntimeError):
@@ -60,8 +62,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_linear_dgrad.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
     lib.fp8_linear_wgrad.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]
     lib.fp8_pad_tokens.argtypes = [_vp, _i64, _i64, _i32, _vp, ctypes.POINTER(_i64), _vp]
-    for name in EXPORTS[:6]:
-        getattr(lib, name).restype = _int
+    _p64, _p32 = ctypes.POINTER(_i64), ctypes.POINTER(_i32)
+    lib.fp8_align_multiple.argtypes = [_int, _i64, _i32, _i32, _i32, _p32, _p32]
+    lib.fp8_pad_varlen.argtypes = [_vp, _p64, _i32, _i64, _i32, _i32, _vp, _p64, _p64, _vp]
+    lib.fp8_unpad_varlen.argtypes = [_vp, _p64, _p64, _i32, _i64, _vp, _vp]
+    for name in EXPORTS:
+        if name not in ("fp8_last_error", "fp8_version"):
+            getattr(lib, name).restype = _int
     lib.fp8_last_error.restype = ctypes.c_char_p
     lib.fp8_last_error.argtypes = []
     lib.fp8_version.restype = ctypes.c_char_p
@@ -288,6 +295,62 @@ def fp8_pad_tokens(x, T=None, multiple=16, x_pad=None, query_only=False, stream=
     _check("fp8_pad_tokens", lib.fp8_pad_tokens(_ptr(_bf16(x)), T, cols, int(multiple),
                                                 _ptr(x_pad), ctypes.byref(out), _stream(stream)))
     return x_pad, T_pad
+
+
+def fp8_align_multiple(layout, batch=1, tp=1, cp=1, base=16):
+    """(per-sequence multiple, total multiple) of a token layout (FP8_LAYOUT_THD or
+    FP8_LAYOUT_BSHD) under tensor/sequence (tp) and context (cp) parallelism."""
+    seq, tot = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("fp8_align_multiple", load().fp8_align_multiple(
+        int(layout), int(batch), int(tp), int(cp), int(base), ctypes.byref(seq),
+        ctypes.byref(tot)))
+    return seq.value, tot.value
+
+
+def _offsets(cu):
+    arr = (_i64 * len(cu))(*[int(v) for v in cu])
+    return arr
+
+
+def fp8_pad_varlen(x, cu_seqlens, seq_multiple=1, total_multiple=16, x_pad=None,
+                   query_only=False, stream=None):
+    """Pad every sequence of a packed bf16 [T, cols] batch to a multiple of ``seq_multiple``
+    rows and the batch to a multiple of ``total_multiple``. ``cu_seqlens``: host offsets
+    [nseq + 1] (a list, or a CPU tensor). Returns ``(x_pad, cu_seqlens_pad, T_pad)``;
+    ``query_only`` computes the offsets only (x_pad is None)."""
+    cu = _offsets([int(v) for v in cu_seqlens])
+    nseq = len(cu) - 1
+    cols = x.shape[1]
+    cu_pad = (_i64 * (nseq + 1))()
+    T_pad = ctypes.c_int64(0)
+    lib = load()
+    _check("fp8_pad_varlen", lib.fp8_pad_varlen(None, cu, nseq, cols, int(seq_multiple),
+                                                int(total_multiple), None, cu_pad,
+                                                ctypes.byref(T_pad), None))
+    if query_only:
+        return None, list(cu_pad), T_pad.value
+    if x_pad is None:
+        x_pad = torch.empty((T_pad.value, cols), dtype=x.dtype, device=x.device)
+    if x_pad.shape[0] < T_pad.value or x_pad.shape[1] != cols:
+        raise ValueError(f"x_pad must be [{T_pad.value}, {cols}]")
+    _check("fp8_pad_varlen", lib.fp8_pad_varlen(_ptr(_bf16(x)), cu, nseq, cols,
+                                                int(seq_multiple), int(total_multiple),
+                                                _ptr(x_pad), cu_pad, ctypes.byref(T_pad),
+                                                _stream(stream)))
+    return x_pad, list(cu_pad), T_pad.value
+
+
+def fp8_unpad_varlen(x_pad, cu_seqlens, cu_seqlens_pad, x=None, stream=None):
+    """The inverse gather of fp8_pad_varlen: the sequences' rows of x_pad, packed."""
+    cu = _offsets([int(v) for v in cu_seqlens])
+    cu_pad = _offsets([int(v) for v in cu_seqlens_pad])
+    nseq = len(cu) - 1
+    cols = x_pad.shape[1]
+    if x is None:
+        x = torch.empty((int(cu[nseq]), cols), dtype=x_pad.dtype, device=x_pad.device)
+    _check("fp8_unpad_varlen", load().fp8_unpad_varlen(_ptr(_bf16(x_pad)), cu, cu_pad, nseq,
+                                                      cols, _ptr(x), _stream(stream)))
+    return x
 
 
 def fp8_last_error() -> str:

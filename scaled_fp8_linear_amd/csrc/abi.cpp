@@ -271,4 +271,108 @@ int fp8_pad_tokens(const void* x, int64_t T, int64_t cols, int32_t multiple, voi
                     fn);
 }
 
+int fp8_align_multiple(int layout, int64_t batch, int32_t tp, int32_t cp, int32_t base,
+                       int32_t* seq_multiple, int32_t* total_multiple) {
+  const char* fn = "fp8_align_multiple";
+  if (!seq_multiple || !total_multiple) return fail(FP8_ERR_NULL, "%s: NULL output", fn);
+  if (batch < 1 || tp < 1 || cp < 1 || base < 1)
+    return fail(FP8_ERR_SHAPE, "%s: batch, tp, cp and base must be positive", fn);
+  auto gcd = [](int64_t a, int64_t b) {
+    while (b) { const int64_t t = a % b; a = b; b = t; }
+    return a;
+  };
+  int64_t seq = 1, total = 1;
+  if (layout == FP8_LAYOUT_THD) {
+    seq = cp > 1 ? 2 * (int64_t)cp : 1;
+    total = (int64_t)base * cp * tp;
+  } else if (layout == FP8_LAYOUT_BSHD) {
+    if (cp != 1)
+      return fail(FP8_ERR_UNSUPPORTED, "%s: BSHD alignment covers tensor/sequence parallelism only",
+                  fn);
+    const int64_t bt = (int64_t)base * tp;
+    const int64_t need = bt / gcd(batch, bt);
+    seq = tp / gcd(tp, need) * need;                  // lcm(tp, need)
+  } else {
+    return fail(FP8_ERR_UNSUPPORTED, "%s: unknown layout %d", fn, layout);
+  }
+  if (seq > 0x7FFFFFFF || total > 0x7FFFFFFF)
+    return fail(FP8_ERR_SHAPE, "%s: multiple does not fit 32 bits", fn);
+  *seq_multiple = (int32_t)seq;
+  *total_multiple = (int32_t)total;
+  return ok();
+}
+
+namespace {
+
+// cu: nseq + 1 non-decreasing host offsets starting at 0.
+int check_offsets(const char* fn, const int64_t* cu, int32_t nseq, const char* what) {
+  if (!cu) return fail(FP8_ERR_NULL, "%s: %s is NULL", fn, what);
+  if (cu[0] != 0) return fail(FP8_ERR_SHAPE, "%s: %s[0] must be 0", fn, what);
+  for (int32_t i = 0; i < nseq; ++i)
+    if (cu[i + 1] < cu[i])
+      return fail(FP8_ERR_SHAPE, "%s: %s decreases at %d", fn, what, i);
+  return FP8_OK;
+}
+
+}  // namespace
+
+int fp8_pad_varlen(const void* x, const int64_t* cu_seqlens, int32_t nseq, int64_t cols,
+                   int32_t seq_multiple, int32_t total_multiple, void* x_pad,
+                   int64_t* cu_seqlens_pad, int64_t* T_pad, void* stream) {
+  const char* fn = "fp8_pad_varlen";
+  if (!T_pad) return fail(FP8_ERR_NULL, "%s: T_pad is NULL", fn);
+  if (nseq < 0 || cols < 0) return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
+  if (seq_multiple < 1 || total_multiple < 1)
+    return fail(FP8_ERR_SHAPE, "%s: multiples must be >= 1", fn);
+  if (cols % 16) return fail(FP8_ERR_SHAPE, "%s: cols=%lld not a multiple of 16", fn, (long long)cols);
+  int e = check_offsets(fn, cu_seqlens, nseq, "cu_seqlens");
+  if (e) return e;
+  // padded offsets on the host
+  int64_t end = 0;
+  int64_t* pad_off = cu_seqlens_pad;
+  for (int32_t i = 0; i <= nseq; ++i) {
+    if (i > 0) {
+      const int64_t len = cu_seqlens[i] - cu_seqlens[i - 1];
+      end += len + ((-len) % seq_multiple + seq_multiple) % seq_multiple;
+    }
+    if (pad_off) pad_off[i] = end;
+  }
+  *T_pad = end + ((-end) % total_multiple + total_multiple) % total_multiple;
+  if (!x_pad) return ok();
+  if (!pad_off) return fail(FP8_ERR_NULL, "%s: cu_seqlens_pad is needed with x_pad", fn);
+  if (*T_pad == 0 || cols == 0) return ok();                 // nothing to write
+  if (x == x_pad) return fail(FP8_ERR_UNSUPPORTED, "%s: x_pad must not be x", fn);
+  if (cu_seqlens[nseq] * cols > 0 && !x) return fail(FP8_ERR_NULL, "%s: x is NULL", fn);
+  if (!aligned16(x) || !aligned16(x_pad))
+    return fail(FP8_ERR_ALIGN, "%s: x and x_pad must be 16-byte aligned", fn);
+  return hip_status(fp8lin::launch_pad_varlen(true, static_cast<const uint16_t*>(x),
+                                              static_cast<uint16_t*>(x_pad), cols, cu_seqlens,
+                                              pad_off, nseq, *T_pad, as_stream(stream)),
+                    fn);
+}
+
+int fp8_unpad_varlen(const void* x_pad, const int64_t* cu_seqlens, const int64_t* cu_seqlens_pad,
+                     int32_t nseq, int64_t cols, void* x, void* stream) {
+  const char* fn = "fp8_unpad_varlen";
+  if (nseq < 0 || cols < 0) return fail(FP8_ERR_SHAPE, "%s: negative size", fn);
+  if (cols % 16) return fail(FP8_ERR_SHAPE, "%s: cols=%lld not a multiple of 16", fn, (long long)cols);
+  int e = check_offsets(fn, cu_seqlens, nseq, "cu_seqlens");
+  if (e) return e;
+  e = check_offsets(fn, cu_seqlens_pad, nseq, "cu_seqlens_pad");
+  if (e) return e;
+  for (int32_t i = 0; i < nseq; ++i)
+    if (cu_seqlens_pad[i + 1] - cu_seqlens_pad[i] < cu_seqlens[i + 1] - cu_seqlens[i])
+      return fail(FP8_ERR_SHAPE, "%s: padded sequence %d is shorter than the sequence", fn, i);
+  if (cu_seqlens[nseq] * cols == 0) return ok();
+  if (!x || !x_pad) return fail(FP8_ERR_NULL, "%s: NULL tensor", fn);
+  if (x == x_pad) return fail(FP8_ERR_UNSUPPORTED, "%s: x must not be x_pad", fn);
+  if (!aligned16(x) || !aligned16(x_pad))
+    return fail(FP8_ERR_ALIGN, "%s: x and x_pad must be 16-byte aligned", fn);
+  return hip_status(fp8lin::launch_pad_varlen(false, static_cast<const uint16_t*>(x_pad),
+                                              static_cast<uint16_t*>(x), cols, cu_seqlens,
+                                              cu_seqlens_pad, nseq, cu_seqlens_pad[nseq],
+                                              as_stream(stream)),
+                    fn);
+}
+
 }  // extern "C"

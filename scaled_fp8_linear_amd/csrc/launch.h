@@ -33,6 +33,17 @@ hipError_t launch_scale_update(int mode, float* amax, bool clear_amax, float* hi
 hipError_t launch_pad_tokens(const uint16_t* x, int64_t T, int64_t cols, int64_t T_pad,
                              uint16_t* x_pad, hipStream_t s);
 
+// Sequences per launch of the per-sequence padding kernel (its row offsets travel in the
+// kernel arguments).
+constexpr int kSeqPerLaunch = 128;
+
+// pad: x [cu[nseq], cols] -> x_pad [T_pad, cols] (sequence i at row cu_pad[i], zero rows
+// after it up to cu_pad[i + 1], zero rows from cu_pad[nseq] to T_pad); !pad: the inverse
+// gather x_pad -> x. cu, cu_pad: host offsets [nseq + 1]; cols % 8 == 0, 16-byte aligned rows.
+hipError_t launch_pad_varlen(bool pad, const uint16_t* in, uint16_t* out, int64_t cols,
+                             const int64_t* cu, const int64_t* cu_pad, int32_t nseq,
+                             int64_t T_pad, hipStream_t s);
+
 // D[m,n] = bf16(scale * sum_k A[m,k] * B[n,k] (+ bias[n])); A [M,K], B [N,K], D [M,N].
 // Tensorwise: scale = sa[0] * sb[0]; bias bf16 [N] or nullptr. Block: sa [M, K/128];
 // sb [N/b_rows, K/128] with b_rows = 128 (weight tiles) or 1 (1x128 tiles); no bias.

@@ -118,3 +118,48 @@ def test_e5m2_flag_checks(lib):
     assert lib.fp8_linear_fwd_bias(p, p, p, p, p, p, 16, 16, 16, 16, 0x200, None) == 4
     # the flag passes the host checks (shape errors are still reported as such)
     assert lib.fp8_linear_wgrad(p, p, p, p, p, 24, 16, 16, 0x200, None) == 2
+
+
+def test_align_multiple_matches_the_oracle(lib):
+    import scaled_fp8_linear_amd as m
+    from oracle import padding
+    for B in (1, 3, 6, 16, 32):
+        for tp in (1, 2, 3, 4, 8):
+            for base in (8, 16):
+                assert m.fp8_align_multiple(m.FP8_LAYOUT_BSHD, B, tp, 1, base) == \
+                    padding.align_multiples(padding.BSHD, B, tp, 1, base), (B, tp, base)
+    for tp in (1, 2, 4):
+        for cp in (1, 2, 4):
+            assert m.fp8_align_multiple(m.FP8_LAYOUT_THD, 1, tp, cp) == \
+                padding.align_multiples(padding.THD, 1, tp, cp)
+    s, t = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.fp8_align_multiple(1, 4, 2, 2, 16, ctypes.byref(s), ctypes.byref(t)) == 4
+    assert lib.fp8_align_multiple(7, 4, 2, 1, 16, ctypes.byref(s), ctypes.byref(t)) == 4
+    assert lib.fp8_align_multiple(0, 4, 0, 1, 16, ctypes.byref(s), ctypes.byref(t)) == 2
+
+
+def test_pad_varlen_offsets_match_the_oracle(lib):
+    import numpy as np
+
+    import scaled_fp8_linear_amd as m
+    import torch
+    from oracle import padding
+    rng = np.random.default_rng(11)
+    lens = [int(v) for v in rng.integers(0, 50, 40)]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = torch.empty((int(cu[-1]), 16), dtype=torch.bfloat16)      # host tensor: offsets only
+    for sm, tm in ((1, 16), (4, 16), (8, 128), (3, 5)):
+        _, cu_pad, T_pad = m.fp8_pad_varlen(x, cu, sm, tm, query_only=True)
+        want, ocu = padding.pad_varlen(np.zeros((int(cu[-1]), 1), np.uint16), lens, sm, tm)
+        assert cu_pad == list(ocu) and T_pad == want.shape[0], (sm, tm)
+    bad = (ctypes.c_int64 * 3)(0, 5, 3)
+    out = ctypes.c_int64()
+    assert lib.fp8_pad_varlen(None, bad, 2, 16, 1, 16, None, None, ctypes.byref(out), None) == 2
+    good = (ctypes.c_int64 * 3)(0, 5, 9)
+    assert lib.fp8_pad_varlen(None, good, 2, 24, 1, 16, None, None, ctypes.byref(out), None) == 2
+    assert lib.fp8_pad_varlen(None, good, 2, 16, 0, 16, None, None, ctypes.byref(out), None) == 2
+    p = ctypes.c_void_p(16)
+    assert lib.fp8_pad_varlen(p, good, 2, 16, 4, 16, p, None, ctypes.byref(out), None) == 1
+    # a padded sequence shorter than its sequence
+    short = (ctypes.c_int64 * 3)(0, 4, 8)
+    assert lib.fp8_unpad_varlen(p, good, short, 2, 16, ctypes.c_void_p(32), None) == 2
