@@ -46,7 +46,9 @@ def _parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 512 MiB buffer three times (for scaling HBM byte counters)")
     ap.add_argument("--data-sensitivity", action="store_true",
-                    help="only time the 8192x4096x14336 GEMM on random, constant and zero codes")
+                    help="only time one GEMM shape on random, constant and zero codes")
+    ap.add_argument("--shape", default="8192,4096,14336",
+                    help="M,N,K of the --data-sensitivity GEMM")
     return ap.parse_args()
 
 
@@ -64,8 +66,8 @@ def copy_calibration():
                                            "bytes_written_per_copy": nbytes, "copies": 3}}))
 
 
-def data_sensitivity(launches=20):
-    """The same GEMM launch (M=8192, N=4096, K=14336) on three sets of operand codes: codes
+def data_sensitivity(launches=20, shape=(8192, 4096, 14336)):
+    """The same GEMM launch (default M=8192, N=4096, K=14336) on three sets of operand codes: codes
     of normal data (as in the step), all codes 0x38 (1.0) and all codes 0. The instruction
     stream and memory traffic are identical; only the bits the matrix cores and data paths
     toggle differ, so a gap in time is a gap in clock (the chip's power limit)."""
@@ -73,7 +75,7 @@ def data_sensitivity(launches=20):
     import scaled_fp8_linear_amd as m
     m.load()
     dev = torch.device("cuda:0")
-    M, N, K = 8192, 4096, 14336
+    M, N, K = shape
     gen = torch.Generator(device=dev).manual_seed(0)
     one = torch.ones(1, device=dev)
     res = {}
@@ -472,7 +474,7 @@ def main():
         copy_calibration()
         return
     if args.data_sensitivity:
-        data_sensitivity()
+        data_sensitivity(shape=tuple(int(v) for v in args.shape.split(",")))
         return
 
     import torch
