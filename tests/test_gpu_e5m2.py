@@ -165,3 +165,33 @@ def test_layer_steps_with_e5m2_gradients(lib):
         for k in ("w_scale", "w_scale_inv", "x_scale", "x_scale_inv", "g_scale", "g_scale_inv"):
             assert f32_bits(st[k]) == f32_bits(rs[k]), (t, k, st[k], rs[k])
         w = workloads.drift(w, 2, t, 1e-4)
+
+
+@pytest.mark.parametrize("M,N,K,what", [(8192, 4096, 14336, "dgrad of gate/up"),
+                                        (14336, 4096, 8192, "wgrad of gate/up"),
+                                        (4096, 14336, 8192, "wgrad of the down projection"),
+                                        (8192, 14336, 4096, "dgrad of the down projection")])
+def test_full_size_backward_e5m2_sampled(lib, M, N, K, what):
+    """The MLP block's backward launch shapes with E5M2 gradients, in the launch configuration
+    the benchmark times: the gradient quantized to E5M2 on the GPU (bit-exact with the oracle
+    above), the E4M3 operand likewise, 1024 sampled outputs computed one by one by the oracle
+    from the sampled rows."""
+    a = workloads.bf16_tensor("normal", (M, K), 3, 61 + K, 0, std=1e-3)
+    b = workloads.bf16_tensor("student_t", (N, K), 3, 62 + K, 0, nu=3)
+    sa, sai = scale_from_amax(o_amax(a), E5M2_MAX)
+    sb, sbi = scale_from_amax(o_amax(b))
+    note(f"full size e5m2 {what}: quantize operands on the GPU")
+    qa, _, _, _, _ = lib.fp8_quantize_amax(dev_bf16(a), scale_inv=dev_f32(sai), want_q_t=False,
+                                           e5m2=True)
+    qb, _, _, _, _ = lib.fp8_quantize_amax(dev_bf16(b), scale_inv=dev_f32(sbi), want_q_t=False)
+    note(f"full size e5m2 {what}: GEMM {M}x{N}x{K}")
+    y = lib.fp8_linear_dgrad(qa, qb, dev_f32(sa), dev_f32(sb), a_e5m2=True)
+    torch.cuda.synchronize()
+    yh = host_bf16_f64(y)
+    rng = np.random.default_rng(K + 1)
+    for m, n in zip(rng.integers(0, M, 1024), rng.integers(0, N, 1024)):
+        ra = quantize_values(a[m:m + 1], sai, "e5m2")
+        rb = quantize_values(b[n:n + 1], sbi)
+        D = gemm.scaled_gemm(ra, rb, sa, sb, "e5m2")[0, 0]
+        bound = gemm.error_bound(ra, rb, sa, sb, a_fmt="e5m2")[0, 0]
+        assert abs(yh[m, n] - D) <= bound, (what, m, n, yh[m, n], D, bound)
