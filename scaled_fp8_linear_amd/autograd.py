@@ -191,7 +191,8 @@ class Fp8Linear(torch.nn.Module):
         if "lin" not in state:
             self._lin = None
             return
-        self._lin = DelayedScalingLinear(self.weight.device, self.update_interval)
+        self._lin = DelayedScalingLinear(self.weight.device, self.update_interval,
+                                         grad_format=self.grad_format)
         self._lin.load_state_dict(state["lin"])
         self._generation = _state.generation
         self._last_step = int(state["last_step"])

@@ -58,3 +58,21 @@ def test_step_without_backward_keeps_gradient_scale():
     a.cur = 0
     a.end_step(g_updated=False)
     assert a.cur == 1 and a.g_scale[1].item() == 5.0 and a.g_scale_inv[1].item() == pytest.approx(0.2)
+
+
+def test_module_state_keeps_the_gradient_format():
+    """Fp8Linear's saved schedule restores into a layer with the same grad_format (the
+    restored schedule codes gradients in E5M2 again), and is refused by one with the
+    other format."""
+    from scaled_fp8_linear_amd import Fp8Linear
+    a = Fp8Linear(32, 48, grad_format="e5m2")
+    a._lin = DelayedScalingLinear("cpu", grad_format="e5m2")
+    a._lin.step_count, a._lin.idx = 9, 9
+    sd = a.state_dict()
+    b = Fp8Linear(32, 48, grad_format="e5m2")
+    b.load_state_dict(sd)
+    assert b._lin.grad_format == "e5m2" and b._lin.step_count == 9
+    with pytest.raises(ValueError):
+        Fp8Linear(32, 48).load_state_dict(sd)
+    with pytest.raises(ValueError):
+        Fp8Linear(32, 48, grad_format="e4m2")

@@ -185,3 +185,47 @@ def test_module_with_bias(lib, M):
                       gemm.error_bound(b["qg"], f["qw_t"], b["sg"], f["sw"])[:M], f"dx step {t}")
         _scales_equal(layer._lin.state(), ref.state(), f"step {t}")
     lib.fp8_state().reset()
+
+
+def test_module_with_e5m2_gradients(lib):
+    """Fp8Linear(grad_format="e5m2") through torch autograd, 18 steps (across the step-16
+    refresh) at a ragged token count, against the oracle's hybrid-format layer."""
+    M, K, N = 250, 384, 400
+    lib.fp8_state().reset()
+    layer = lib.Fp8Linear(K, N, device="cuda", grad_format="e5m2")
+    ref = DelayedLinear(grad_format="e5m2")
+    Mp = M + (-M) % 16
+    w = workloads.linear_inputs(2, 0, M=Mp, K=K, N=N)["w"]
+    for t in range(1, 19):
+        d = workloads.linear_inputs(2, t, M=Mp, K=K, N=N)
+        x, g = d["x"][:M], d["g"][:M]
+        note(f"Fp8Linear e5m2 step {t}")
+        layer.weight.data.copy_(dev_bf16(w))
+        layer.weight.grad = None
+        xd = dev_bf16(x).requires_grad_(True)
+        with lib.fp8_autocast():
+            y = layer(xd)
+        y.backward(dev_bf16(g))
+        torch.cuda.synchronize()
+        ref.begin_step()
+        f = ref.forward(_pad(x, Mp), w, rows_valid=M)
+        b = ref.backward(_pad(g, Mp))
+        assert_within(host_bf16_f64(y), f["y"][:M],
+                      gemm.error_bound(f["qx"], f["qw"], f["sx"], f["sw"])[:M], f"y step {t}")
+        assert_within(host_bf16_f64(xd.grad), b["dx"][:M],
+                      gemm.error_bound(b["qg"], f["qw_t"], b["sg"], f["sw"], a_fmt="e5m2")[:M],
+                      f"dx step {t}")
+        assert_within(host_bf16_f64(layer.weight.grad), b["dw"],
+                      gemm.error_bound(b["qg_t"], f["qx_t"], b["sg"], f["sx"], a_fmt="e5m2"),
+                      f"dw step {t}")
+        _scales_equal(layer._lin.state(), ref.state(), f"step {t}")
+        w = workloads.drift(w, 2, t, 1e-4)
+    sd = layer.state_dict()
+    same = lib.Fp8Linear(K, N, device="cuda", grad_format="e5m2")
+    same.load_state_dict(sd)
+    assert same._lin.grad_format == "e5m2"
+    _scales_equal(same._lin.state(), ref.state(), "restored")
+    fresh = lib.Fp8Linear(K, N, device="cuda")            # E4M3 gradients: a mismatch
+    with pytest.raises(ValueError):
+        fresh.load_state_dict(sd)
+    lib.fp8_state().reset()
