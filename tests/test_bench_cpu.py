@@ -46,3 +46,25 @@ def test_committed_traffic_is_used_only_for_its_code(tmp_path, monkeypatch):
     assert bench.counter_traffic("other") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", summary("0" * 16))
     assert bench.counter_traffic("k") is None
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    """The hot path runs on one device: --gpus 2 is refused before anything touches a GPU."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_traffic_file_names_existing_sources():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    text = open(os.path.join(root, "profiles", "hbm_traffic_mlp_8192x4096x14336.txt")).read()
+    srcs = [ln.split()[1:] for ln in text.splitlines() if ln.startswith("sources ")]
+    assert len(srcs) == 2
+    for files in srcs:
+        for f in files:
+            assert os.path.exists(os.path.join(root, f)), f
