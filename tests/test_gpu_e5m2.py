@@ -195,3 +195,25 @@ def test_full_size_backward_e5m2_sampled(lib, M, N, K, what):
         D = gemm.scaled_gemm(ra, rb, sa, sb, "e5m2")[0, 0]
         bound = gemm.error_bound(ra, rb, sa, sb, a_fmt="e5m2")[0, 0]
         assert abs(yh[m, n] - D) <= bound, (what, m, n, yh[m, n], D, bound)
+
+
+def test_full_size_gradient_e5m2(lib):
+    """g [8192, 14336] N(0, 1e-3) at the MLP block's size, coded in E5M2 with a stale
+    multiplier (both tails saturate): amax exact over the whole tensor, codes and transposed
+    codes bit-exact on sampled rows and columns."""
+    g = workloads.bf16_tensor("normal", (8192, 14336), 3, workloads.T_G, 0, std=1e-3)
+    oa = o_amax(g)
+    _, si = scale_from_amax(np.float32(oa / 4), E5M2_MAX)
+    note("e5m2 quantize full size [8192,14336]")
+    q, qt, a, _, _ = lib.fp8_quantize_amax(dev_bf16(g), scale_inv=dev_f32(si), e5m2=True)
+    torch.cuda.synchronize()
+    assert f32_bits(a.item()) == f32_bits(oa)
+    rng = np.random.default_rng(9)
+    for r in rng.choice(8192, 16, replace=False):
+        want = quantize_values(g[r], si, "e5m2")
+        assert_same_bytes(host_u8(q[int(r)]), want, f"row {r}")
+    for c in rng.choice(14336, 16, replace=False):
+        want = quantize_values(g[:, c], si, "e5m2")
+        assert_same_bytes(host_u8(qt[int(c)]), want, f"q_t row {c}")
+    qh = host_u8(q)
+    assert (qh == 0x7B).any() and (qh == 0xFB).any()

@@ -111,3 +111,23 @@ def test_bshd_batch_through_the_layer(lib):
         assert_same_bytes(host_bf16_bits(y_packed),
                           padding.unpad_varlen(host_bf16_bits(y), lens, cu_pad), "y unpadded")
         lin.end_step()
+
+
+def test_full_size_packed_batch_as_benchmarked(lib):
+    """The benchmark's launch: the 54 657-token packed batch, 4096 columns, THD with
+    tp = cp = 2 (each sequence to a multiple of 4, the batch to 64), pad and unpad bit-exact
+    with the oracle over every row."""
+    sm, tm = lib.fp8_align_multiple(lib.FP8_LAYOUT_THD, 1, 2, 2)
+    lens = workloads.varlen_lengths(4)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    x = workloads.bf16_tensor("normal", (T, 4096), 4, 98, 0, std=1.0)
+    want, ocu = padding.pad_varlen(x, lens, sm, tm)
+    note(f"full-size pad_varlen T={T} cols=4096")
+    x_pad, cu_pad, T_pad = lib.fp8_pad_varlen(dev_bf16(x), cu, sm, tm)
+    torch.cuda.synchronize()
+    assert cu_pad == list(ocu) and T_pad == want.shape[0] == 54784
+    assert_same_bytes(host_bf16_bits(x_pad), want, "x_pad")
+    back = lib.fp8_unpad_varlen(x_pad, cu, cu_pad)
+    torch.cuda.synchronize()
+    assert_same_bytes(host_bf16_bits(back), x, "unpad")
