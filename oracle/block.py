@@ -128,3 +128,42 @@ def block_error_bound(qa, qb, sa, sb, b_rows_per_scale: int, rel: float = 1e-2):
     da = dequant_rows(qa, sa, 1)
     db = dequant_rows(qb, sb, b_rows_per_scale)
     return rel * np.outer(np.sqrt((da * da).sum(1)), np.sqrt((db * db).sum(1)))
+
+
+def block_fp32_bound(qa, qb, sa, sb, b_rows_per_scale: int):
+    """``(D, bound)``: ``block_scaled_gemm`` and a tight bound on ``|D_gpu - D|`` for a
+    kernel that forms each block's partial sum in float32 from zero (n_b products, any
+    order, partial sums at most ``A_b = sum_{k in b} |a_k b_k|``), multiplies it by the
+    float32 product ``w_b`` of its two scales and adds it to a float32 accumulator (one
+    rounding each for the scale product and the fused multiply-add), then rounds to bf16.
+    With u = 2**-23 (any faithful float32 rounding) and ``Q_b`` the exact result through
+    block b, the accumulator is within
+    ``u * sum_b (|w_b| (n_b + 1) A_b + |Q_b|) / (1 - u (K + blocks))``
+    of D; bf16 rounding adds at most 2**-8 of the value (see ``oracle.gemm``)."""
+    import torch
+    from .gemm import BF16_HALF_ULP, F32_U, FLUSH_FLOOR
+    da = torch.from_numpy(e4m3.decode(qa))
+    db = torch.from_numpy(e4m3.decode(qb))
+    M, K = da.shape
+    N = db.shape[0]
+    assert K % BLOCK == 0 and db.shape[1] == K
+    nb = K // BLOCK
+    sa64 = torch.from_numpy(np.asarray(sa, dtype=np.float32).astype(np.float64))
+    sb64 = torch.from_numpy(np.repeat(np.asarray(sb, dtype=np.float32).astype(np.float64),
+                                      b_rows_per_scale, axis=0))
+    assert tuple(sa64.shape) == (M, nb) and tuple(sb64.shape) == (N, nb)
+    Q = torch.zeros((M, N), dtype=torch.float64)
+    E = torch.zeros((M, N), dtype=torch.float64)
+    W = torch.zeros((M, N), dtype=torch.float64)
+    for kb in range(nb):
+        ks = slice(kb * BLOCK, (kb + 1) * BLOCK)
+        a, b = da[:, ks], db[:, ks]
+        w = torch.outer(sa64[:, kb], sb64[:, kb])   # exact: two 24-bit significands
+        wA = w.abs() * (a.abs() @ b.abs().T)
+        Q.add_(w * (a @ b.T))
+        E.add_(wA * (BLOCK + 1)).add_(Q.abs())
+        W.add_(wA)
+    # float64's own rounding of the products w * S_b and of the running sum
+    e_acc = F32_U * E / (1.0 - F32_U * (K + nb)) + 2.0 ** -50 * nb * W
+    bound = e_acc + BF16_HALF_ULP * (Q.abs() + e_acc) + FLUSH_FLOOR
+    return Q.numpy(), bound.numpy()

@@ -28,6 +28,24 @@ inside the tolerance below.
 Tolerance (the target the GPU result is judged by): per element,
 ``|D_gpu - D| <= 1e-2 * ||dqA[m, :]||_2 * ||dqB[n, :]||_2`` with the
 dequantized operands ``dq = decode(Q) * s`` in float64.
+
+A second, tight bound (``fp32_bound``) follows from the arithmetic the layout
+implies: float32 accumulation over the contraction in blocks of 128 (one
+matrix-core instruction each), the float32 product of the two scales, one
+float32 multiply, and one round to bf16. Unlike the norm tolerance, it is
+small enough to see a single 128-wide block of the contraction dropped or
+counted twice at K = 8192 or 14336. Its derivation, for any order of the
+additions inside a block and any faithful float32 rounding (unit u = 2**-23):
+
+* while block b (n_b products) is added, every partial sum is the accumulator
+  entering the block plus some of the block's products, so its magnitude is
+  at most ``|P_b| + A_b``: ``P_b`` the exact sum of the blocks before b,
+  ``A_b = sum_{k in b} |a_k b_k|`` (to first order in u). A block costs at
+  most n_b roundings, so the accumulator is within
+  ``E = u * sum_b n_b (|P_b| + A_b) / (1 - u K)`` of the exact sum (the
+  divisor covers the errors already in the accumulator);
+* the scale product and the multiply add at most 2**-23 |D| (two roundings of
+  2**-24), and bf16 rounding to nearest even at most 2**-8 of the value.
 """
 from __future__ import annotations
 
@@ -78,3 +96,39 @@ def bf16_round(d: np.ndarray) -> np.ndarray:
     rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
     nan = np.isnan(f)
     return np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), rounded)
+
+
+F32_U = 2.0 ** -23           # one float32 rounding, relative (any faithful rounding)
+BF16_HALF_ULP = 2.0 ** -8    # round to nearest even on bf16's 8-bit significand, relative
+FLUSH_FLOOR = 2.0 ** -126    # absolute: a float32 below the normal range may be flushed
+ACC_BLOCK = 128              # contraction block of one matrix-core instruction
+
+
+def fp32_bound(qa, qb, sa, sb, a_fmt: str = "e4m3", block: int = ACC_BLOCK):
+    """``(D, bound)``: the exact scaled product and the tight float32-accumulation bound
+    on ``|D_gpu - D|`` derived in the module docstring, elementwise in float64.
+
+    The sums run over the contraction in blocks of ``block`` with torch's CPU float64
+    matrix product as the primitive (exact for E4M3 operands, see above)."""
+    import torch
+    da = torch.from_numpy(CODECS[a_fmt].decode(np.asarray(qa, dtype=np.uint8)))
+    db = torch.from_numpy(e4m3.decode(np.asarray(qb, dtype=np.uint8)))
+    M, K = da.shape
+    N = db.shape[0]
+    assert db.shape[1] == K and K < EXACT_K_LIMIT
+    P = torch.zeros((M, N), dtype=torch.float64)       # exact prefix sum
+    E = torch.zeros((M, N), dtype=torch.float64)       # sum_b n_b (|P_b| + A_b)
+    A_tot = torch.zeros((M, N), dtype=torch.float64)
+    for k0 in range(0, K, block):
+        a, b = da[:, k0:k0 + block], db[:, k0:k0 + block]
+        A = a.abs() @ b.abs().T
+        E.add_((P.abs() + A) * a.shape[1])
+        A_tot.add_(A)
+        P.add_(a @ b.T)
+    s = float(np.float64(np.float32(sa)) * np.float64(np.float32(sb)))
+    D = P * s
+    # float64's own rounding (only E5M2 operands can make a block sum inexact)
+    e_acc = F32_U * E / (1.0 - F32_U * K) + 2.0 ** -50 * K * A_tot
+    b1 = abs(s) * e_acc * (1.0 + 2.0 ** -22) + 2.0 ** -22 * D.abs()
+    bound = b1 + BF16_HALF_ULP * (D.abs() + b1) + FLUSH_FLOOR
+    return D.numpy(), bound.numpy()

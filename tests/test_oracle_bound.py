@@ -1,0 +1,223 @@
+"""Pins of the tight float32-accumulation bounds (``oracle.gemm.fp32_bound``,
+``oracle.block.block_fp32_bound``), on the CPU.
+
+A tolerance is only useful if it is neither too tight nor too loose:
+
+* too tight would fail a correct kernel: float32 emulations of every plausible
+  accumulation (products added one by one in order, in reverse order, rounded toward
+  zero, or block sums joined to the accumulator) must stay inside it, on bench-like data
+  (Student-t(3) activations, N(0, 0.02) weights, N(0, 1e-3) gradients);
+* too loose would pass a broken kernel: results with one 128-wide block of the
+  contraction dropped, counted twice, negated or read from the neighbouring row, or with
+  a wrong scale, must fail it in most elements at K = 4096, 8192 and 14336 (the norm
+  tolerance ``gemm.error_bound`` fails such a result in no element at all at K >= 8192).
+
+The defects are planted in numpy copies of oracle results here, never in a kernel.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import block, e4m3, gemm
+from oracle.quantize import amax, quantize_tensorwise
+from oracle.scaling import scale_from_amax
+
+BLK = 128
+
+
+def _codes(kind, shape, tensor, **p):
+    bits = workloads.bf16_tensor(kind, shape, 90, tensor, 0, **p)
+    s, si = scale_from_amax(amax(bits))
+    q, _, _ = quantize_tensorwise(bits, si)
+    return q, s
+
+
+def _bf16(v32):
+    """float32 -> bf16 value (round to nearest even), as float64."""
+    return gemm.bf16_round(v32).astype(np.uint32).__lshift__(16).view(np.float32).astype(np.float64)
+
+
+def _epilogue(acc32, sa, sb):
+    s32 = np.float32(np.float32(sa) * np.float32(sb))
+    return _bf16(np.float32(acc32) * s32)
+
+
+def _products(qa, qb):
+    da = e4m3.decode(qa).astype(np.float32)
+    db = e4m3.decode(qb).astype(np.float32)
+    return da[:, None, :] * db[None, :, :]            # exact in float32
+
+
+def emulate_sequential(qa, qb, sa, sb, reverse=False):
+    """Every product added to a float32 accumulator one at a time (round to nearest)."""
+    p = _products(qa, qb)
+    if reverse:
+        p = p[..., ::-1]
+    acc = np.add.accumulate(p, axis=2, dtype=np.float32)[..., -1]
+    return _epilogue(acc, sa, sb)
+
+
+def emulate_toward_zero(qa, qb, sa, sb):
+    """As emulate_sequential, but every addition rounds toward zero."""
+    p = _products(qa, qb).astype(np.float64)
+    acc = np.zeros(p.shape[:2], dtype=np.float32)
+    for k in range(p.shape[2]):
+        exact = acc.astype(np.float64) + p[..., k]
+        r = exact.astype(np.float32)
+        over = np.abs(r.astype(np.float64)) > np.abs(exact)
+        acc = np.where(over, np.nextafter(r, np.float32(0)), r).astype(np.float32)
+    return _epilogue(acc, sa, sb)
+
+
+def emulate_two_level(qa, qb, sa, sb):
+    """Each block's exact sum rounded to float32, then added to a float32 accumulator."""
+    da, db = e4m3.decode(qa), e4m3.decode(qb)
+    acc = np.zeros((qa.shape[0], qb.shape[0]), dtype=np.float32)
+    for k0 in range(0, qa.shape[1], BLK):
+        s = np.float32(da[:, k0:k0 + BLK] @ db[:, k0:k0 + BLK].T)
+        acc = (acc + s).astype(np.float32)
+    return _epilogue(acc, sa, sb)
+
+
+OPERANDS = {
+    # forward: Student-t(3) activations x N(0, 0.02) weights
+    "fwd": (("student_t", dict(nu=3)), ("normal", dict(std=0.02))),
+    # dgrad / wgrad: N(0, 1e-3) gradients x weights / activations
+    "bwd": (("normal", dict(std=1e-3)), ("student_t", dict(nu=3))),
+}
+
+
+def _case(K, which, M=24, N=20):
+    (ka, pa), (kb, pb) = OPERANDS[which]
+    qa, sa = _codes(ka, (M, K), 1 + K, **pa)
+    qb, sb = _codes(kb, (N, K), 2 + K, **pb)
+    return qa, qb, sa, sb
+
+
+@pytest.mark.parametrize("K", [256, 4096, 14336])
+@pytest.mark.parametrize("which", ["fwd", "bwd"])
+def test_float32_kernels_pass(K, which):
+    qa, qb, sa, sb = _case(K, which, M=12, N=10)
+    D, bound = gemm.fp32_bound(qa, qb, sa, sb)
+    assert np.array_equal(D, gemm.scaled_gemm(qa, qb, sa, sb))
+    for name, got in (("sequential", emulate_sequential(qa, qb, sa, sb)),
+                      ("reversed", emulate_sequential(qa, qb, sa, sb, reverse=True)),
+                      ("two-level", emulate_two_level(qa, qb, sa, sb))):
+        ratio = np.abs(got - D) / bound
+        assert ratio.max() <= 1.0, (name, K, which, ratio.max())
+    if K <= 4096:
+        got = emulate_toward_zero(qa, qb, sa, sb)
+        assert (np.abs(got - D) / bound).max() <= 1.0, ("toward zero", K, which)
+
+
+def test_bound_is_tight_where_rounding_is_forced():
+    """Sums that float32 cannot hold: 2**24 plus 128 products of 0.5 (each addition a tie
+    that rounds back to 2**24 when added one by one). The sequential emulation loses 64,
+    and the bound must allow that; it must not allow 4 times as much."""
+    K = 256
+    qa = np.zeros((1, K), np.uint8)
+    qb = np.zeros((1, K), np.uint8)
+    # block 0: 128 products 448 * 256 * ... -> use 1.0 x 1.0 = 1 to build 128, scaled by codes
+    qa[0, :BLK] = 0x7E                  # 448
+    qb[0, :BLK] = 0x7E                  # 448 -> 128 * 200704 = 25690112 (> 2**24)
+    qa[0, BLK:] = 0x30                  # 0.5
+    qb[0, BLK:] = 0x38                  # 1.0 -> 128 products of 0.5
+    D, bound = gemm.fp32_bound(qa, qb, 1.0, 1.0)
+    assert D[0, 0] == 25690112 + 64
+    seq = emulate_sequential(qa, qb, 1.0, 1.0)[0, 0]
+    assert abs(seq - D[0, 0]) <= bound[0, 0]
+    # bf16 output: spacing 2**17 here, so the bound is dominated by the output rounding
+    assert bound[0, 0] < 2.0 ** -8 * D[0, 0] * 1.1
+
+
+DEFECTS = ["drop_first", "drop_middle", "drop_last", "double", "negate", "neighbour_row",
+           "scale_x2"]
+
+
+def _plant(qa, qb, sa, sb, D, defect):
+    """D with one defect planted (all arithmetic exact, in float64)."""
+    K = qa.shape[1]
+    nb = K // BLK
+    j = {"drop_first": 0, "drop_last": nb - 1}.get(defect, nb // 2 + 1)
+    s = np.float64(np.float32(sa)) * np.float64(np.float32(sb))
+    da, db = e4m3.decode(qa), e4m3.decode(qb)
+    ks = slice(j * BLK, (j + 1) * BLK)
+    Sj = s * (da[:, ks] @ db[:, ks].T)
+    if defect.startswith("drop"):
+        return D - Sj
+    if defect == "double":
+        return D + Sj
+    if defect == "negate":
+        return D - 2 * Sj
+    if defect == "neighbour_row":         # block j of B read from row n + 1
+        return D - Sj + s * (da[:, ks] @ np.roll(db, -1, axis=0)[:, ks].T)
+    if defect == "scale_x2":
+        return 2 * D
+    raise ValueError(defect)
+
+
+@pytest.mark.parametrize("K", [4096, 8192, 14336])
+@pytest.mark.parametrize("which", ["fwd", "bwd"])
+def test_planted_defects_fail(K, which):
+    qa, qb, sa, sb = _case(K, which)
+    D, bound = gemm.fp32_bound(qa, qb, sa, sb)
+    norm_bound = gemm.error_bound(qa, qb, sa, sb)
+    for defect in DEFECTS:
+        bad = _bf16(np.float32(_plant(qa, qb, sa, sb, D, defect)))   # as a kernel would store it
+        flagged = np.mean(np.abs(bad - D) > bound)
+        assert flagged >= 0.8, (defect, K, which, flagged)
+        if K >= 8192 and defect.startswith("drop"):
+            # the norm tolerance cannot see it: the reason for the second bound
+            assert np.mean(np.abs(bad - D) > norm_bound) < 0.01, (defect, K, which)
+
+
+# ---------------------------------------------------------------- block recipe
+def _block_case(K, b_rows, M=16, N=256):
+    xa = workloads.bf16_tensor("outlier_normal", (BLK, K), 91, K, 0, rate=0.01, mult=100.0)
+    xb = workloads.bf16_tensor("outlier_normal", (N, K), 91, K + 1, 0, rate=0.01, mult=100.0)
+    qa, _, _, sa, _ = block.quantize_1x128(xa)      # 1x128 tiles: the first M rows are exact
+    qa, sa = qa[:M], sa[:M]
+    if b_rows == 1:
+        qb, _, _, sb, _ = block.quantize_1x128(xb)
+    else:
+        qb, _, _, sb, _ = block.quantize_128x128(xb)
+    return qa, qb, sa, sb
+
+
+def emulate_block(qa, qb, sa, sb, b_rows, sequential):
+    """Per block: the partial sum in float32 from zero (products one by one, or the exact
+    block sum rounded once), times the float32 scale product, added with one rounding."""
+    da, db = e4m3.decode(qa), e4m3.decode(qb)
+    sbr = np.repeat(np.asarray(sb, np.float32), b_rows, axis=0)
+    acc = np.zeros((qa.shape[0], qb.shape[0]), dtype=np.float32)
+    for kb in range(qa.shape[1] // BLK):
+        ks = slice(kb * BLK, (kb + 1) * BLK)
+        if sequential:
+            p = (da[:, None, ks] * db[None, :, ks]).astype(np.float32)
+            P = np.add.accumulate(p, axis=2, dtype=np.float32)[..., -1]
+        else:
+            P = np.float32(da[:, ks] @ db[:, ks].T)
+        f = np.float32(np.asarray(sa, np.float32)[:, kb][:, None] * sbr[:, kb][None, :])
+        acc = (P.astype(np.float64) * f.astype(np.float64) + acc.astype(np.float64)).astype(np.float32)
+    return _bf16(acc)
+
+
+@pytest.mark.parametrize("b_rows", [128, 1])
+@pytest.mark.parametrize("K", [1024, 8192])
+def test_block_bound(K, b_rows):
+    qa, qb, sa, sb = _block_case(K, b_rows)
+    D, bound = block.block_fp32_bound(qa, qb, sa, sb, b_rows)
+    assert np.allclose(D, block.block_scaled_gemm(qa, qb, sa, sb, b_rows), rtol=1e-15, atol=0)
+    for seq in (True, False):
+        got = emulate_block(qa, qb, sa, sb, b_rows, seq)
+        assert (np.abs(got - D) / bound).max() <= 1.0, (K, b_rows, seq)
+    # one block dropped / doubled: flagged in most elements
+    sbr = np.repeat(np.asarray(sb, np.float32).astype(np.float64), b_rows, axis=0)
+    da, db = e4m3.decode(qa), e4m3.decode(qb)
+    j = K // BLK // 2
+    ks = slice(j * BLK, (j + 1) * BLK)
+    Sj = np.outer(np.asarray(sa, np.float32)[:, j].astype(np.float64), sbr[:, j]) * \
+        (da[:, ks] @ db[:, ks].T)
+    for bad in (D - Sj, D + Sj):
+        flagged = np.mean(np.abs(_bf16(np.float32(bad)) - D) > bound)
+        assert flagged >= 0.8, (K, b_rows, flagged)
