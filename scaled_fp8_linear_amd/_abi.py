@@ -99,19 +99,23 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+_CODE_DTYPES = (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2)
+_BF16_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+
 def _codes(t):
-    """uint8 view of an e4m3 code tensor (uint8 or float8_e4m3fn storage)."""
+    """uint8 view of an fp8 code tensor (uint8, float8_e4m3fn or float8_e5m2 storage)."""
     if t is None:
         return None
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         return t.view(torch.uint8)
     if t.dtype != torch.uint8:
-        raise ValueError(f"e4m3 codes must be uint8 or float8_e4m3fn, got {t.dtype}")
+        raise ValueError(f"fp8 codes must be uint8 or float8 storage, got {t.dtype}")
     return t
 
 
 def _bf16(t):
-    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+    if t.dtype not in _BF16_DTYPES:
         raise ValueError(f"expected a bf16 tensor, got {t.dtype}")
     return t
 
@@ -127,6 +131,8 @@ class Slot:
 
     def __init__(self, tensor, index: int = 0):
         _f32(tensor, "slot")
+        if not 0 <= int(index) < tensor.numel():
+            raise ValueError(f"slot {index} is outside a tensor of {tensor.numel()} elements")
         self.tensor, self.index = tensor, int(index)
 
     def ptr(self):
@@ -141,6 +147,53 @@ def _fptr(v, name):
     return _ptr(_f32(v, name))
 
 
+def _need(t, name, shape, dtypes, dev=None):
+    """Check a buffer before its address goes to the library: dtype, exact shape,
+    contiguity and device (``dev``: the device of the call's first operand). Raises
+    ValueError; nothing has been enqueued at that point."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, the operands on {dev}")
+
+
+def _need_scalar(v, name, dev=None, count=1):
+    """A float32 scale or amax: a Slot, or a tensor of at least ``count`` elements."""
+    if v is None:
+        return
+    t = v.tensor if isinstance(v, Slot) else v
+    _f32(t, name)
+    if not isinstance(v, Slot) and t.numel() < count:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {count}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, the operands on {dev}")
+
+
+def _need_scales(v, name, gran, grid, dev):
+    """Tensorwise: one float32 scale; block recipe: the scale grid of that exact shape."""
+    if gran & 0xFF == FP8_TENSORWISE:
+        _need_scalar(v, name, dev)
+    else:
+        if isinstance(v, Slot):
+            raise ValueError(f"{name}: the block recipe takes a scale grid, not a slot")
+        _need(v, name, grid, (torch.float32,), dev)
+
+
+def _grids(gran, rows, cols):
+    """Shapes of (amax, scale, scale_t) for a block-recipe quantize of [rows, cols]."""
+    if gran == FP8_BLOCK_1x128:
+        return (rows, cols // 128), (rows, cols // 128), (cols, rows // 128)
+    return (rows // 128, cols // 128), (rows // 128, cols // 128), (cols // 128, rows // 128)
+
+
 def fp8_quantize_amax(x, rows_valid=None, gran=FP8_TENSORWISE, scale_inv=None, q=None, q_t=None,
                       amax=None, scale=None, scale_t=None, want_q=True, want_q_t=True,
                       want_amax=True, amax_accumulate=False, e5m2=False, stream=None):
@@ -153,9 +206,24 @@ def fp8_quantize_amax(x, rows_valid=None, gran=FP8_TENSORWISE, scale_inv=None, q
     if amax_accumulate and amax is None:
         raise ValueError("amax_accumulate needs the amax tensor to fold into")
     _bf16(x)
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [rows, cols], got shape {tuple(x.shape)}")
     rows, cols = x.shape
     rv = rows if rows_valid is None else int(rows_valid)
     dev = x.device
+    q, q_t = _codes(q), _codes(q_t)
+    _need(q, "q", (rows, cols), _CODE_DTYPES, dev)
+    _need(q_t, "q_t", (cols, rows), _CODE_DTYPES, dev)
+    if gran == FP8_TENSORWISE:
+        _need_scalar(scale_inv, "scale_inv", dev)
+        _need_scalar(amax, "amax", dev)
+        if scale is not None or scale_t is not None:
+            raise ValueError("tensorwise quantize takes no scale grids")
+    elif gran in (FP8_BLOCK_1x128, FP8_BLOCK_128x128):
+        ga, gs, gst = _grids(gran, rows, cols)
+        _need(amax, "amax", ga, (torch.float32,), dev)
+        _need(scale, "scale", gs, (torch.float32,), dev)
+        _need(scale_t, "scale_t", gst, (torch.float32,), dev)
     if want_q and q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if want_q_t and q_t is None:
@@ -163,18 +231,14 @@ def fp8_quantize_amax(x, rows_valid=None, gran=FP8_TENSORWISE, scale_inv=None, q
     if gran == FP8_TENSORWISE:
         if want_amax and amax is None:
             amax = torch.empty(1, dtype=torch.float32, device=dev)
-    else:
-        grid_r = rows // 128
+    elif gran in (FP8_BLOCK_1x128, FP8_BLOCK_128x128):
+        ga, gs, gst = _grids(gran, rows, cols)
         if want_amax and amax is None:
-            amax = torch.empty((rows if gran == FP8_BLOCK_1x128 else grid_r, cols // 128),
-                               dtype=torch.float32, device=dev)
+            amax = torch.empty(ga, dtype=torch.float32, device=dev)
         if q is not None and scale is None:
-            scale = torch.empty((rows if gran == FP8_BLOCK_1x128 else grid_r, cols // 128),
-                                dtype=torch.float32, device=dev)
+            scale = torch.empty(gs, dtype=torch.float32, device=dev)
         if q_t is not None and scale_t is None:
-            scale_t = torch.empty((cols if gran == FP8_BLOCK_1x128 else cols // 128, grid_r),
-                                  dtype=torch.float32, device=dev)
-    q, q_t = _codes(q), _codes(q_t)
+            scale_t = torch.empty(gst, dtype=torch.float32, device=dev)
     _check("fp8_quantize_amax", load().fp8_quantize_amax(
         _ptr(x), rows, cols, rv,
         gran | (FP8_AMAX_ACCUMULATE if amax_accumulate else 0) | (FP8_E5M2 if e5m2 else 0),
@@ -188,30 +252,58 @@ def fp8_scale_update(mode, amax=None, hist=None, pos=0, scale=None, scale_inv=No
     """One scale bookkeeping op on the device (see fp8lin.h for the modes).
     ``clear_amax``: set amax to +0 after reading it (FROM_AMAX, RECORD).
     ``e5m2``: scales for E5M2 codes (57344 in place of 448; FROM_AMAX, REFRESH)."""
+    if hist is not None:
+        _f32(hist, "hist")
+        if hist.dim() != 1 or not hist.is_contiguous():
+            raise ValueError("hist must be a contiguous 1-D float32 tensor")
     length = 0 if hist is None else hist.numel()
+    for v, name in ((amax, "amax"), (scale, "scale"), (scale_inv, "scale_inv")):
+        _need_scalar(v, name)
     flags = (FP8_SCALE_CLEAR_AMAX if clear_amax else 0) | (FP8_E5M2 if e5m2 else 0)
     _check("fp8_scale_update", load().fp8_scale_update(
         int(mode) | flags, _fptr(amax, "amax"), _fptr(hist, "hist"), length, int(pos),
         _fptr(scale, "scale"), _fptr(scale_inv, "scale_inv"), _stream(stream)))
 
 
+def _operands(a, b, an, bn):
+    """Two code operands with the contraction index last; returns (a, b) as uint8 views."""
+    a, b = _codes(a), _codes(b)
+    for t, name in ((a, an), (b, bn)):
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-D code tensor")
+    if b.device != a.device:
+        raise ValueError(f"{bn} is on {b.device}, {an} on {a.device}")
+    if a.shape[1] != b.shape[1]:
+        raise ValueError(f"{an} {tuple(a.shape)} and {bn} {tuple(b.shape)}: contraction sizes "
+                         "differ")
+    return a, b
+
+
+def _m_valid(M_valid, M):
+    mv = M if M_valid is None else int(M_valid)
+    if not 0 <= mv <= M:
+        raise ValueError(f"M_valid={mv} outside [0, {M}]")
+    return mv
+
+
 def fp8_linear_fwd(qx, qw, sx, sw, y=None, M_valid=None, gran=FP8_TENSORWISE, stream=None,
                    bias=None, a_e5m2=False):
     """y [M, N] bf16 = sx * sw * qx [M, K] . qw [N, K]^T (+ bias [N], bf16, in the epilogue).
     ``a_e5m2``: qx holds E5M2 codes."""
-    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
-    qx, qw = _codes(qx), _codes(qw)
+    qx, qw = _operands(qx, qw, "qx", "qw")
     M, K = qx.shape
     N = qw.shape[0]
-    if qw.shape[1] != K:
-        raise ValueError("qx and qw contraction sizes differ")
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
-    mv = M if M_valid is None else int(M_valid)
+    dev = qx.device
+    _need_scales(sx, "sx", gran, (M, K // 128), dev)
+    _need_scales(sw, "sw", gran, (N // 128, K // 128), dev)
+    _need(y, "y", (M, N), _BF16_DTYPES, dev)
     if bias is not None:
-        _bf16(bias)
-        if tuple(bias.shape) != (N,):
-            raise ValueError(f"bias must be [{N}]")
+        _need(_bf16(bias), "bias", (N,), _BF16_DTYPES, dev)
+    mv = _m_valid(M_valid, M)
+    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if bias is not None:
         _check("fp8_linear_fwd_bias", load().fp8_linear_fwd_bias(
             _ptr(qx), _ptr(qw), _fptr(sx, "sx"), _fptr(sw, "sw"), _ptr(bias), _ptr(y), M, N, K,
             mv, gran, _stream(stream)))
@@ -225,8 +317,11 @@ def fp8_linear_fwd(qx, qw, sx, sw, y=None, M_valid=None, gran=FP8_TENSORWISE, st
 def fp8_bias_grad(g, rows_valid=None, db=None, stream=None):
     """db [cols] bf16 = column sums of g [rows, cols] over the valid rows (float32 sums)."""
     _bf16(g)
+    if g.dim() != 2:
+        raise ValueError(f"g must be 2-D [rows, cols], got shape {tuple(g.shape)}")
     rows, cols = g.shape
-    rv = rows if rows_valid is None else int(rows_valid)
+    rv = _m_valid(rows_valid, rows)
+    _need(db, "db", (cols,), _BF16_DTYPES, g.device)
     if db is None:
         db = torch.empty(cols, dtype=torch.bfloat16, device=g.device)
     _check("fp8_bias_grad", load().fp8_bias_grad(_ptr(g), rows, cols, rv, _ptr(db),
@@ -236,16 +331,19 @@ def fp8_bias_grad(g, rows_valid=None, db=None, stream=None):
 
 def fp8_linear_dgrad(qg, qw_t, sg, sw, dx=None, M_valid=None, gran=FP8_TENSORWISE, stream=None,
                      a_e5m2=False):
-    """dx [M, K] bf16 = sg * sw * qg [M, N] . qw_t [K, N]^T. ``a_e5m2``: qg holds E5M2 codes."""
-    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
-    qg, qw_t = _codes(qg), _codes(qw_t)
+    """dx [M, K] bf16 = sg * sw * qg [M, N] . qw_t [K, N]^T. ``a_e5m2``: qg holds E5M2 codes.
+    Block recipe: sg [M, N/128], sw is W's transposed scale grid [K/128, N/128]."""
+    qg, qw_t = _operands(qg, qw_t, "qg", "qw_t")
     M, N = qg.shape
     K = qw_t.shape[0]
-    if qw_t.shape[1] != N:
-        raise ValueError("qg and qw_t contraction sizes differ")
+    dev = qg.device
+    _need_scales(sg, "sg", gran, (M, N // 128), dev)
+    _need_scales(sw, "sw", gran, (K // 128, N // 128), dev)
+    _need(dx, "dx", (M, K), _BF16_DTYPES, dev)
+    mv = _m_valid(M_valid, M)
+    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
     if dx is None:
-        dx = torch.empty((M, K), dtype=torch.bfloat16, device=qg.device)
-    mv = M if M_valid is None else int(M_valid)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     _check("fp8_linear_dgrad", load().fp8_linear_dgrad(
         _ptr(qg), _ptr(qw_t), _fptr(sg, "sg"), _fptr(sw, "sw"), _ptr(dx), M, N, K, mv, gran,
         _stream(stream)))
@@ -255,15 +353,17 @@ def fp8_linear_dgrad(qg, qw_t, sg, sw, dx=None, M_valid=None, gran=FP8_TENSORWIS
 def fp8_linear_wgrad(qg_t, qx_t, sg, sx, dw=None, gran=FP8_TENSORWISE, stream=None,
                      a_e5m2=False):
     """dw [N, K] bf16 = sg * sx * qg_t [N, M] . qx_t [K, M]^T. ``a_e5m2``: qg_t holds E5M2
-    codes."""
-    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
-    qg_t, qx_t = _codes(qg_t), _codes(qx_t)
+    codes. Block recipe: sg [N, M/128], sx [K, M/128] (the transposed copies' grids)."""
+    qg_t, qx_t = _operands(qg_t, qx_t, "qg_t", "qx_t")
     N, M = qg_t.shape
     K = qx_t.shape[0]
-    if qx_t.shape[1] != M:
-        raise ValueError("qg_t and qx_t contraction sizes differ")
+    dev = qg_t.device
+    _need_scales(sg, "sg", gran, (N, M // 128), dev)
+    _need_scales(sx, "sx", gran, (K, M // 128), dev)
+    _need(dw, "dw", (N, K), _BF16_DTYPES, dev)
+    gran = gran | (FP8_A_E5M2 if a_e5m2 else 0)
     if dw is None:
-        dw = torch.empty((N, K), dtype=torch.bfloat16, device=qg_t.device)
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     _check("fp8_linear_wgrad", load().fp8_linear_wgrad(
         _ptr(qg_t), _ptr(qx_t), _fptr(sg, "sg"), _fptr(sx, "sx"), _ptr(dw), M, N, K, gran,
         _stream(stream)))
@@ -277,22 +377,31 @@ def fp8_pad_tokens(x, T=None, multiple=16, x_pad=None, query_only=False, stream=
     ``x_pad is x`` the tail of x's own buffer (which must hold T_pad rows) is
     zeroed in place, with T given explicitly.
     """
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [rows, cols], got shape {tuple(x.shape)}")
     cols = x.shape[1]
     T = x.shape[0] if T is None else int(T)
     out = ctypes.c_int64(0)
     lib = load()
-    if query_only:
-        _check("fp8_pad_tokens", lib.fp8_pad_tokens(None, T, cols, int(multiple), None,
-                                                    ctypes.byref(out), None))
-        return None, out.value
     _check("fp8_pad_tokens", lib.fp8_pad_tokens(None, T, cols, int(multiple), None,
                                                 ctypes.byref(out), None))
     T_pad = out.value
+    if query_only:
+        return None, T_pad
+    _bf16(x)
+    if x_pad is x:
+        if x.shape[0] < T_pad:
+            raise ValueError(f"in place: the buffer holds {x.shape[0]} rows, needs {T_pad}")
+    elif x.shape[0] < T:
+        raise ValueError(f"x holds {x.shape[0]} rows, T={T}")
     if x_pad is None:
         x_pad = torch.empty((T_pad, cols), dtype=x.dtype, device=x.device)
-    if x_pad.shape[0] < T_pad:
-        raise ValueError(f"x_pad holds {x_pad.shape[0]} rows, needs {T_pad}")
-    _check("fp8_pad_tokens", lib.fp8_pad_tokens(_ptr(_bf16(x)), T, cols, int(multiple),
+    _bf16(x_pad)
+    if x_pad.dim() != 2 or x_pad.shape[0] < T_pad or x_pad.shape[1] != cols:
+        raise ValueError(f"x_pad has shape {tuple(x_pad.shape)}, needs at least [{T_pad}, {cols}]")
+    if x_pad.device != x.device:
+        raise ValueError("x_pad and x are on different devices")
+    _check("fp8_pad_tokens", lib.fp8_pad_tokens(_ptr(x), T, cols, int(multiple),
                                                 _ptr(x_pad), ctypes.byref(out), _stream(stream)))
     return x_pad, T_pad
 
@@ -320,6 +429,8 @@ def fp8_pad_varlen(x, cu_seqlens, seq_multiple=1, total_multiple=16, x_pad=None,
     ``query_only`` computes the offsets only (x_pad is None)."""
     cu = _offsets([int(v) for v in cu_seqlens])
     nseq = len(cu) - 1
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [rows, cols], got shape {tuple(x.shape)}")
     cols = x.shape[1]
     cu_pad = (_i64 * (nseq + 1))()
     T_pad = ctypes.c_int64(0)
@@ -329,11 +440,18 @@ def fp8_pad_varlen(x, cu_seqlens, seq_multiple=1, total_multiple=16, x_pad=None,
                                                 ctypes.byref(T_pad), None))
     if query_only:
         return None, list(cu_pad), T_pad.value
+    _bf16(x)
+    if x.shape[0] < cu[nseq]:
+        raise ValueError(f"x holds {x.shape[0]} rows, the offsets reach {cu[nseq]}")
     if x_pad is None:
         x_pad = torch.empty((T_pad.value, cols), dtype=x.dtype, device=x.device)
-    if x_pad.shape[0] < T_pad.value or x_pad.shape[1] != cols:
-        raise ValueError(f"x_pad must be [{T_pad.value}, {cols}]")
-    _check("fp8_pad_varlen", lib.fp8_pad_varlen(_ptr(_bf16(x)), cu, nseq, cols,
+    _bf16(x_pad)
+    if x_pad.dim() != 2 or x_pad.shape[0] < T_pad.value or x_pad.shape[1] != cols:
+        raise ValueError(f"x_pad has shape {tuple(x_pad.shape)}, needs at least "
+                         f"[{T_pad.value}, {cols}]")
+    if x_pad.device != x.device:
+        raise ValueError("x_pad and x are on different devices")
+    _check("fp8_pad_varlen", lib.fp8_pad_varlen(_ptr(x), cu, nseq, cols,
                                                 int(seq_multiple), int(total_multiple),
                                                 _ptr(x_pad), cu_pad, ctypes.byref(T_pad),
                                                 _stream(stream)))
@@ -345,10 +463,23 @@ def fp8_unpad_varlen(x_pad, cu_seqlens, cu_seqlens_pad, x=None, stream=None):
     cu = _offsets([int(v) for v in cu_seqlens])
     cu_pad = _offsets([int(v) for v in cu_seqlens_pad])
     nseq = len(cu) - 1
+    if len(cu_pad) != nseq + 1:
+        raise ValueError("cu_seqlens and cu_seqlens_pad differ in length")
+    _bf16(x_pad)
+    if x_pad.dim() != 2:
+        raise ValueError(f"x_pad must be 2-D [rows, cols], got shape {tuple(x_pad.shape)}")
     cols = x_pad.shape[1]
+    if x_pad.shape[0] < cu_pad[nseq]:
+        raise ValueError(f"x_pad holds {x_pad.shape[0]} rows, the padded offsets reach "
+                         f"{cu_pad[nseq]}")
     if x is None:
         x = torch.empty((int(cu[nseq]), cols), dtype=x_pad.dtype, device=x_pad.device)
-    _check("fp8_unpad_varlen", load().fp8_unpad_varlen(_ptr(_bf16(x_pad)), cu, cu_pad, nseq,
+    _bf16(x)
+    if x.dim() != 2 or x.shape[0] < cu[nseq] or x.shape[1] != cols:
+        raise ValueError(f"x has shape {tuple(x.shape)}, needs at least [{cu[nseq]}, {cols}]")
+    if x.device != x_pad.device:
+        raise ValueError("x and x_pad are on different devices")
+    _check("fp8_unpad_varlen", load().fp8_unpad_varlen(_ptr(x_pad), cu, cu_pad, nseq,
                                                       cols, _ptr(x), _stream(stream)))
     return x
 
