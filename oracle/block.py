@@ -136,12 +136,13 @@ def block_fp32_bound(qa, qb, sa, sb, b_rows_per_scale: int):
     order, partial sums at most ``A_b = sum_{k in b} |a_k b_k|``), multiplies it by the
     float32 product ``w_b`` of its two scales and adds it to a float32 accumulator (one
     rounding each for the scale product and the fused multiply-add), then rounds to bf16.
-    With u = 2**-23 (any faithful float32 rounding) and ``Q_b`` the exact result through
-    block b, the accumulator is within
-    ``u * sum_b (|w_b| (n_b + 1) A_b + |Q_b|) / (1 - u (K + blocks))``
-    of D; bf16 rounding adds at most 2**-8 of the value (see ``oracle.gemm``)."""
+    With u = 2**-23 (any faithful float32 rounding), ``Q_b`` the exact result through
+    block b and ``T_b`` the block's group-truncation term of ``oracle.gemm`` (the matrix
+    instruction's aligned groups of 8), the accumulator is within
+    ``sum_b |w_b| (u (n_b + 1) A_b + 2**-10 T_b) + u sum_b |Q_b|``, over
+    ``1 - u (K + blocks)``, of D; bf16 rounding adds at most 2**-8 of the value."""
     import torch
-    from .gemm import BF16_HALF_ULP, F32_U, FLUSH_FLOOR
+    from .gemm import BF16_HALF_ULP, F32_U, FLUSH_FLOOR, GROUP_LOSS, MATRIX_GROUP, group_pow2_max
     da = torch.from_numpy(e4m3.decode(qa))
     db = torch.from_numpy(e4m3.decode(qb))
     M, K = da.shape
@@ -152,18 +153,24 @@ def block_fp32_bound(qa, qb, sa, sb, b_rows_per_scale: int):
     sb64 = torch.from_numpy(np.repeat(np.asarray(sb, dtype=np.float32).astype(np.float64),
                                       b_rows_per_scale, axis=0))
     assert tuple(sa64.shape) == (M, nb) and tuple(sb64.shape) == (N, nb)
+    ga = torch.from_numpy(group_pow2_max(qa))
+    gb = torch.from_numpy(group_pow2_max(qb))
+    gpb = BLOCK // MATRIX_GROUP                    # groups per block
     Q = torch.zeros((M, N), dtype=torch.float64)
     E = torch.zeros((M, N), dtype=torch.float64)
+    G = torch.zeros((M, N), dtype=torch.float64)
     W = torch.zeros((M, N), dtype=torch.float64)
     for kb in range(nb):
         ks = slice(kb * BLOCK, (kb + 1) * BLOCK)
+        gs = slice(kb * gpb, (kb + 1) * gpb)
         a, b = da[:, ks], db[:, ks]
         w = torch.outer(sa64[:, kb], sb64[:, kb])   # exact: two 24-bit significands
         wA = w.abs() * (a.abs() @ b.abs().T)
         Q.add_(w * (a @ b.T))
         E.add_(wA * (BLOCK + 1)).add_(Q.abs())
+        G.add_(w.abs() * (ga[:, gs] @ gb[:, gs].T))
         W.add_(wA)
     # float64's own rounding of the products w * S_b and of the running sum
-    e_acc = F32_U * E / (1.0 - F32_U * (K + nb)) + 2.0 ** -50 * nb * W
+    e_acc = F32_U * E / (1.0 - F32_U * (K + nb)) + GROUP_LOSS * G + 2.0 ** -50 * nb * W
     bound = e_acc + BF16_HALF_ULP * (Q.abs() + e_acc) + FLUSH_FLOOR
     return Q.numpy(), bound.numpy()
