@@ -43,8 +43,6 @@
 //  * epilogue: v_cvt_pk_bf16_f32 packs, a lane permute pairs results so that every
 //    lane stores 16 contiguous bytes through a buffer resource (pieces outside D are
 //    dropped by its range check); rows at or past M_valid are written as zeros.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "common.h"
@@ -1231,17 +1229,19 @@ gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-bool env_flag(const char* name, bool dflt) {
-  const char* e = getenv(name);
-  return e ? atoi(e) != 0 : dflt;
-}
-
-int forced_cfg() {
-  static int v = [] {
-    const char* e = getenv("FP8LIN_GEMM_CFG");
-    return e ? atoi(e) : -1;
-  }();
-  return v;
+// One rectangle of output tiles per XCD (workgroups are dispatched round-robin over the 8
+// XCDs): of the splits of the tile grid into pm x pn = 8 equal rectangles, the one whose
+// rectangle spans the fewest A + B panel rows, so the tiles running together on an XCD
+// share the most operand bytes in its L2. No split (0, 0) if none divides the grid.
+void xcd_split(int tiles_m, int tiles_n, int bm, int bn, int& split_m, int& split_n) {
+  int best = 1 << 30;
+  split_m = split_n = 0;
+  for (int pm = 1; pm <= 8; pm *= 2) {
+    const int pn = 8 / pm;
+    if (tiles_m % pm || tiles_n % pn) continue;
+    const int cost = (tiles_m / pm) * bm + (tiles_n / pn) * bn;
+    if (cost < best) { best = cost; split_m = pm; split_n = pn; }
+  }
 }
 
 template <class C>
@@ -1269,16 +1269,7 @@ hipError_t run_persist(const uint8_t* A, const uint8_t* B, const float* sa, cons
   const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
   // one rectangle of tiles per XCD: the split with the fewest A+B panel rows per XCD
   int split_m = 0, split_n = 0;
-  static const bool split_on = env_flag("FP8LIN_GEMM_XCD_SPLIT", true);
-  if (grid == kMaxWorkgroups && split_on) {
-    int best = 1 << 30;
-    for (int pm = 1; pm <= 8; pm *= 2) {
-      const int pn = 8 / pm;
-      if (tiles_m % pm || tiles_n % pn) continue;
-      const int cost = (tiles_m / pm) * C::BM + (tiles_n / pn) * C::BN;
-      if (cost < best) { best = cost; split_m = pm; split_n = pn; }
-    }
-  }
+  if (grid == kMaxWorkgroups) xcd_split(tiles_m, tiles_n, C::BM, C::BN, split_m, split_n);
   hipLaunchKernelGGL(gemm_fp8_persist_kernel<C>, dim3((unsigned)grid), dim3(C::kThreads), 0, s, A,
                      B, sa, sb, bias, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   return hipGetLastError();
@@ -1313,16 +1304,7 @@ hipError_t run_mx16(const uint8_t* A, const uint8_t* B, const float* sa, const f
   const int tiles = tiles_m * tiles_n;
   const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
   int split_m = 0, split_n = 0;
-  static const bool split_on = env_flag("FP8LIN_GEMM_XCD_SPLIT", true);
-  if (grid == kMaxWorkgroups && split_on) {
-    int best = 1 << 30;
-    for (int pm = 1; pm <= 8; pm *= 2) {
-      const int pn = 8 / pm;
-      if (tiles_m % pm || tiles_n % pn) continue;
-      const int cost = (tiles_m / pm) * C::BM + (tiles_n / pn) * C::BN;
-      if (cost < best) { best = cost; split_m = pm; split_n = pn; }
-    }
-  }
+  if (grid == kMaxWorkgroups) xcd_split(tiles_m, tiles_n, C::BM, C::BN, split_m, split_n);
   const dim3 g((unsigned)grid), b(C::kThreads);
   const bool tail = K % (2 * kStageK) != 0;
   if (bias == nullptr && !tail)
@@ -1360,16 +1342,7 @@ hipError_t run_mx16b(const uint8_t* A, const uint8_t* B, const float* sa, const 
   const int tiles = tiles_m * tiles_n;
   const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
   int split_m = 0, split_n = 0;
-  static const bool split_on = env_flag("FP8LIN_GEMM_XCD_SPLIT", true);
-  if (grid == kMaxWorkgroups && split_on) {
-    int best = 1 << 30;
-    for (int pm = 1; pm <= 8; pm *= 2) {
-      const int pn = 8 / pm;
-      if (tiles_m % pm || tiles_n % pn) continue;
-      const int cost = (tiles_m / pm) * C::BM + (tiles_n / pn) * C::BN;
-      if (cost < best) { best = cost; split_m = pm; split_n = pn; }
-    }
-  }
+  if (grid == kMaxWorkgroups) xcd_split(tiles_m, tiles_n, C::BM, C::BN, split_m, split_n);
   // an odd count of K blocks ends each tile with a padding stage (stages come in pairs)
   if ((K / kStageK) % 2 == 0)
     hipLaunchKernelGGL((gemm_fp8_mx16b_kernel<C, false>), dim3((unsigned)grid), dim3(C::kThreads),
@@ -1390,9 +1363,7 @@ hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const 
                      uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
   // K is a multiple of 128 (checked on the host), so the step count is even
   // (the per-row B scale variant keeps two stages: four run out of registers)
-  static const int forced = forced_cfg();
-  if (K >= 4 * kStageK && forced != 0)
-    return run_mx16b<BlkMx16<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
+  if (K >= 4 * kStageK) return run_mx16b<BlkMx16<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
   const int nk = K / kBKS;
   if constexpr (BROWS != 1)
     if (nk % 4 == 0)
@@ -1403,17 +1374,14 @@ hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const 
 // Tensorwise dispatch for one A format.
 // The 16x16x128 kernel for K of at least 512 when the output spans at least 64 of its
 // tiles; else the 32x32x64 persistent kernel with 256x256 tiles, or 128x128 tiles for
-// small outputs. FP8LIN_GEMM_CFG (0: 256x256, 1: 128x128, 2: 16x16x128) forces a choice
-// for sweeps.
+// small outputs.
 template <int AF>
 hipError_t run_tensorwise_fmt(const uint8_t* A, const uint8_t* B, const float* sa,
                               const float* sb, const uint16_t* bias, uint16_t* D, int m, int n,
                               int k, int mv, hipStream_t s) {
   const bool mx16_ok = k >= 4 * kStageK;
   const bool big = (int64_t)m * n >= (int64_t)2048 * 2048;
-  int cfg = forced_cfg();
-  if (cfg < 0) cfg = big ? (mx16_ok ? 2 : 0) : 1;
-  if (cfg == 2 && mx16_ok) {
+  if (big && mx16_ok) {
     // Beyond one round of 256x256 tiles, the tile shape with the shortest makespan:
     // rounds of kMaxWorkgroups tiles times the tile's area (896 tiles of 256x256 take 4
     // rounds, the last half empty; 1024 of 224x256 take 4 full ones, each 7/8 as long).
@@ -1429,7 +1397,7 @@ hipError_t run_tensorwise_fmt(const uint8_t* A, const uint8_t* B, const float* s
     }
     return run_mx16<TwMx16<AF>>(A, B, sa, sb, bias, D, m, n, k, mv, s);
   }
-  if (cfg == 1)
+  if (!big)
     return run_tensorwise<TwSmall<AF>, TwSmall2<AF>>(A, B, sa, sb, bias, D, m, n, k, mv, s);
   return run_tensorwise<TwBig<AF>, TwBig2<AF>>(A, B, sa, sb, bias, D, m, n, k, mv, s);
 }

@@ -22,8 +22,6 @@
 //    and NaN patterns sort above infinity), reduced across the wavefront with
 //    shuffles, across the workgroup in LDS, and published with ONE atomicMax
 //    per workgroup on the float bits (non-negative floats order as integers).
-#include <stdlib.h>
-
 #include "common.h"
 #include "launch.h"
 
@@ -98,12 +96,9 @@ quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t
   constexpr int kPasses = QC::kPasses;
   constexpr int kRPP = QC::kRowsPerPass;
 
-  // All loads of the lane (4 per pass) go out before any is used. Rows past rows_valid and
-  // columns past cols are loaded from a clamped (valid) address and zeroed after the
-  // load, so the loads need no branches; rows_valid >= 1 here (the host skips empty
-  // tensors and tiles with no valid row read nothing).
-  const int64_t last_row = rows_valid - 1;
-  const int64_t lcol = col_ok ? col : cols - 8;
+  // All loads of the lane (4 per pass) go out before any is used. Rows past rows_valid
+  // (token padding) and columns past cols are not read: those lanes skip the load and
+  // hold zeros.
   uint4 v[kPasses][4];
   bool ok[kPasses][4];
 #pragma unroll
@@ -112,15 +107,13 @@ quantize_tensorwise_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t
     for (int i = 0; i < 4; ++i) {
       const int64_t r = row0 + kRPP * p + 4 * rg + i;
       ok[p][i] = col_ok && (r < rows_valid);
-      const int64_t lr = r < rows_valid ? r : last_row;
-      v[p][i] = ld16<NT>(x + lr * cols + lcol);
+      v[p][i] = ok[p][i] ? ld16<NT>(x + r * cols + col) : make_uint4(0, 0, 0, 0);
     }
   uint32_t mx = 0;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (!ok[p][i]) v[p][i] = make_uint4(0, 0, 0, 0);
       const uint32_t m0 = v[p][i].x & 0x7FFF7FFFu, m1 = v[p][i].y & 0x7FFF7FFFu;
       const uint32_t m2 = v[p][i].z & 0x7FFF7FFFu, m3 = v[p][i].w & 0x7FFF7FFFu;
       const uint32_t a = max(max(m0 & 0xFFFFu, m0 >> 16), max(m1 & 0xFFFFu, m1 >> 16));
@@ -230,14 +223,6 @@ hipError_t run_q(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_val
   return hipGetLastError();
 }
 
-int quant_cfg() {
-  static int v = [] {
-    const char* e = getenv("FP8LIN_QUANT_CFG");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-
 }  // namespace
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
@@ -270,20 +255,16 @@ hipError_t launch_quantize_tensorwise(const uint16_t* x, int64_t rows, int64_t c
       return e;
     return hipSuccess;
   }
-  // Default: 128 x 256 tiles for 1024 lanes (one pass: four 16-byte loads per lane, 16
-  // waves per workgroup); streaming loads and q stores, ordinary q_t stores. q_t leaves as
-  // 128-byte pieces of rows that lie `rows` bytes apart; streaming stores send each piece
-  // to HBM alone, which costs a third of the rate on tall tensors (54672 x 4096: 3.4
-  // against 4.7 TB/s), while the cached path merges neighbouring pieces first. Measured
-  // per shape against 256 lanes (four passes): 5-15% faster (x [8192, 4096] 28.3 -> 26.9
-  // us, W [14336, 4096] 47.9 -> 42.2, g [8192, 14336] 96.3 -> 90.1, [54672, 4096] 194 ->
-  // 165); 512 lanes fall in between.
-  switch (quant_cfg()) {
-    case 1: return run_q<QCfg<128, 256, 256, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
-    case 2: return run_q<QCfg<128, 256, 512, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
-    case 3: return run_q<QCfg<128, 256, 1024, 7>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
-    default: return run_q<QCfg<128, 256, 1024, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax, e5m2, s);
-  }
+  // 128 x 256 tiles for 1024 lanes (one pass: four 16-byte loads per lane, 16 waves per
+  // workgroup); streaming loads and q stores, ordinary q_t stores. q_t leaves as 128-byte
+  // pieces of rows that lie `rows` bytes apart; streaming stores send each piece to HBM
+  // alone, which costs a third of the rate on tall tensors (54672 x 4096: 3.4 against
+  // 4.7 TB/s), while the cached path merges neighbouring pieces first. Measured per shape
+  // against 256 lanes (four passes): 5-15% faster (x [8192, 4096] 28.3 -> 26.9 us,
+  // W [14336, 4096] 47.9 -> 42.2, g [8192, 14336] 96.3 -> 90.1, [54672, 4096] 194 -> 165);
+  // 512 lanes fall in between.
+  return run_q<QCfg<128, 256, 1024, 3>>(x, rows, cols, rows_valid, scale_inv, q, q_t, amax,
+                                        e5m2, s);
 }
 
 }  // namespace fp8lin

@@ -44,6 +44,14 @@ def _exact_and_bound(qa, qb, sa, sb):
     return gemm.scaled_gemm(qa, qb, sa, sb), gemm.error_bound(qa, qb, sa, sb)
 
 
+def _within_both(got, qa, qb, sa, sb, what):
+    """The tolerance of record and the tight float32-accumulation bound (oracle.gemm)."""
+    D, tight = gemm.fp32_bound(qa, qb, sa, sb)
+    worst = assert_within(got, D, gemm.error_bound(qa, qb, sa, sb), what)
+    assert_within(got, D, tight, f"{what} (float32 accumulation)")
+    return worst
+
+
 SHAPES = [(64, 128, 128), (16, 16, 16), (528, 784, 656), (256, 256, 4096), (1040, 272, 1008),
           (4096 + 16, 512, 144)]
 
@@ -199,9 +207,17 @@ def test_wide_kernel_ragged(lib, M, N, K, mv):
     torch.cuda.synchronize()
     yh = host_bf16_f64(y)
     assert np.all(yh[mv:] == 0)
-    D, b = _exact_and_bound(qa[:mv], qb, sa, sb)
-    worst = assert_within(yh[:mv], D, b, f"fwd {M}x{N}x{K}")
+    worst = _within_both(yh[:mv], qa[:mv], qb, sa, sb, f"fwd {M}x{N}x{K}")
     assert worst < 0.25
+
+
+# Outputs of at least 2048 x 2048 with a contraction shorter than 512 take the 32x32x64
+# kernel with 256x256 tiles: four-stage ring (K/64 a multiple of 4), two-stage ring (even),
+# and one tile per workgroup (odd K/64); ragged rows and padded rows included.
+@pytest.mark.parametrize("M,N,K,mv", [(2048, 2048, 256, 2048), (2064, 2048, 384, 2000),
+                                      (2048, 2304, 128, 2048), (2064, 2048, 144, 2050)])
+def test_wide_output_short_contraction(lib, M, N, K, mv):
+    test_wide_kernel_ragged(lib, M, N, K, mv)
 
 
 @pytest.mark.parametrize("M,N,K,mv", [
