@@ -185,71 +185,208 @@ class EventProbe:
         return [a.elapsed_time(b) for a, b in self.pairs.get(tag, [])]
 
 
-def cpu_baseline(sample_tokens: int) -> dict:
-    """The CPU oracle, as it is, on a bounded sample of the same workload.
+def _oracle_quantize_slabs(bits, scale_inv, pool, slabs):
+    """The oracle's tensorwise quantize of a bf16 [rows, cols] tensor, cut into row slabs
+    that run on a thread pool (numpy releases the GIL inside its array operations); the
+    transposed copy is put together from the slabs' transposes."""
+    from oracle.quantize import quantize_tensorwise
+    rows = bits.shape[0]
+    bounds = np.linspace(0, rows, slabs + 1).astype(int)
+    parts = list(pool.map(lambda i: quantize_tensorwise(bits[bounds[i]:bounds[i + 1]], scale_inv),
+                          range(slabs)))
+    q = np.concatenate([p[0] for p in parts])
+    q_t = np.concatenate([p[1] for p in parts], axis=1)
+    return q, q_t
 
-    Sample: the gate linear (K=4096, N=14336) restricted to ``sample_tokens`` tokens
-    (quantize x and g slabs, forward/dgrad/wgrad of the slab in float64) plus the
-    quantize of a 1024-row slab of W; scaled linearly to the full step of three linears
-    (up and down have the same FLOPs and element counts as gate).
+
+def cpu_baseline(sample_tokens: int) -> dict:
+    """The CPU oracle, as it is, on the benchmark's own step: the three linears of the MLP
+    block (gate, up: 4096 -> 14336; down: 14336 -> 4096), each with amax, scale and quantize
+    of its input, weight and output gradient (the oracle's quantize on row slabs, one per
+    host core, in threads) and forward, dgrad and wgrad in float64 through numpy's BLAS.
+    ``sample_tokens`` below 8192 restricts every linear to that many tokens and scales the
+    time linearly (for slow hosts); at 8192 nothing is extrapolated.
     """
+    from concurrent.futures import ThreadPoolExecutor
+
     import workloads
     from oracle import gemm
-    from oracle.quantize import quantize_tensorwise
-    from oracle.scaling import scale_from_amax
     from oracle.quantize import amax as o_amax
+    from oracle.scaling import scale_from_amax
 
     M, K, N = 8192, 4096, 14336
-    S, R = sample_tokens, 1024
-    x = workloads.bf16_tensor("student_t", (S, K), 3, workloads.T_X, 0, nu=3)
-    g = workloads.bf16_tensor("normal", (S, N), 3, workloads.T_GGATE, 0, std=1e-3)
-    w = workloads.bf16_tensor("normal", (R, K), 3, workloads.T_WGATE, 0, std=0.02)
+    S = min(sample_tokens, M)
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas_threads = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    _, swi = scale_from_amax(o_amax(w))
-    qw_slab, _, _ = quantize_tensorwise(w, swi)
-    t_w = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    sx, sxi = scale_from_amax(o_amax(x))
-    sg, sgi = scale_from_amax(o_amax(g))
-    qx, qx_t, _ = quantize_tensorwise(x, sxi)
-    qg, qg_t, _ = quantize_tensorwise(g, sgi)
-    t_q = time.perf_counter() - t0
-    # the slab's three GEMMs against a full-size weight (codes tiled from the slab)
-    qw = np.tile(qw_slab, (N // R, 1))
-    qw_t = np.ascontiguousarray(qw.T)
-    t0 = time.perf_counter()
-    gemm.scaled_gemm(qx, qw, sx, 1.0)              # forward  [S, N], contraction K
-    gemm.scaled_gemm(qg, qw_t, sg, 1.0)            # dgrad    [S, K], contraction N
-    gemm.scaled_gemm(qg_t, qx_t, sg, sx)           # wgrad    [N, K], contraction over S tokens
-    t_g = time.perf_counter() - t0
-    t_linear = t_w * (N / R) + (t_q + t_g) * (M / S)
-    t_step = 3 * t_linear
+        blas_threads = cores
+    ST, W02, G13 = dict(nu=3), dict(std=0.02), dict(std=1e-3)
+    linears = {   # x, W, g of each linear, drawn as the GPU step draws them
+        "gate": (("student_t", (S, K), workloads.T_X, ST), ("normal", (N, K), workloads.T_WGATE, W02),
+                 ("normal", (S, N), workloads.T_GGATE, G13)),
+        "up": (("student_t", (S, K), workloads.T_X, ST), ("normal", (N, K), workloads.T_WUP, W02),
+               ("normal", (S, N), workloads.T_GUP, G13)),
+        "down": (("student_t", (S, N), workloads.T_H, ST), ("normal", (K, N), workloads.T_WDOWN, W02),
+                 ("normal", (S, K), workloads.T_GDOWN, G13)),
+    }
+    t_q = t_g = 0.0
+    elems = 0
+    with ThreadPoolExecutor(cores) as pool:
+        for spec in linears.values():
+            bits = [workloads.bf16_tensor(kind, shape, 3, tid, 0, **p)
+                    for kind, shape, tid, p in spec]
+            t0 = time.perf_counter()
+            qs = []
+            for b in bits:
+                s_, si = scale_from_amax(o_amax(b))
+                qs.append((s_,) + _oracle_quantize_slabs(b, si, pool, cores))
+                elems += b.size
+            t_q += time.perf_counter() - t0
+            (sx, qx, qx_t), (sw, qw, qw_t), (sg, qg, qg_t) = qs
+            t0 = time.perf_counter()
+            gemm.scaled_gemm(qx, qw, sx, sw)            # forward, contraction over inputs
+            gemm.scaled_gemm(qg, qw_t, sg, sw)          # dgrad, contraction over outputs
+            gemm.scaled_gemm(qg_t, qx_t, sg, sx)        # wgrad, contraction over tokens
+            t_g += time.perf_counter() - t0
+            del bits, qs
+    t_step = (t_q + t_g) * (M / S)
     flops = 3 * 6.0 * M * N * K
     return {"value": round(flops / t_step / 1e12, 6), "unit": "TFLOP/s",
-            "cores": int(blas_threads), "kind": "oracle",
-            "sample": (f"gate linear on {S} of {M} tokens (quantize x,g slabs; fwd, dgrad, wgrad in "
-                       f"float64 via BLAS with {blas_threads} threads) + quantize of {R} of {N} "
-                       f"weight rows (single-threaded numpy), scaled linearly to the 3-linear step; "
-                       f"measured {t_w + t_q + t_g:.1f} s, extrapolated step {t_step:.1f} s")}
+            "cores": int(max(cores, blas_threads)), "kind": "oracle",
+            "affinity_cores": cores, "blas_threads": int(blas_threads), "quantize_threads": cores,
+            "quantize_gbs": round(4.0 * elems / t_q / 1e9, 3),
+            "gemm_gflops": round(3 * 3 * 2.0 * S * N * K / t_g / 1e9, 1),
+            "sample": (f"the whole step on {S} of {M} tokens: quantize of x, W, g of the 3 "
+                       f"linears (oracle, {cores} row slabs on {cores} threads) and their fwd, "
+                       f"dgrad, wgrad in float64 (BLAS, {blas_threads} threads); measured "
+                       f"{t_q + t_g:.1f} s (quantize {t_q:.1f} s, GEMMs {t_g:.1f} s)"
+                       + ("" if S == M else f", scaled x{M / S:g} to the full step"))}
 
 
-def _time_steps(torch, step, steps, warmup):
-    for _ in range(warmup):
-        step()
+def measure_config1(torch, m, workloads, iters=200, repeats=7):
+    """Config 1: one fp8 linear forward with current tensorwise scaling, x [64, 128],
+    W [128, 128], N(0, 1): for each operand an amax pass, the scale from that amax (no
+    delay), the cast with it; then the GEMM (7 launches). Latency per forward, as launched
+    eagerly from Python and as one captured HIP graph (replayed; checked byte for byte
+    against the eager result)."""
+    d = workloads.linear_inputs(1)
+    dev = torch.device("cuda:0")
+
+    def up(b):
+        return torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w = up(d["x"]), up(d["w"])
+    f32 = dict(dtype=torch.float32, device=dev)
+    amax = {n: torch.zeros(1, **f32) for n in "xw"}
+    sc = {n: torch.ones(1, **f32) for n in "xw"}
+    si = {n: torch.ones(1, **f32) for n in "xw"}
+    q = {"x": torch.empty((64, 128), dtype=torch.uint8, device=dev),
+         "w": torch.empty((128, 128), dtype=torch.uint8, device=dev)}
+    y = torch.empty((64, 128), dtype=torch.bfloat16, device=dev)
+    src = {"x": x, "w": w}
+
+    def forward():
+        for n in "xw":
+            # amax folded into a cleared buffer; the scale update reads it and clears it
+            m.fp8_quantize_amax(src[n], amax=amax[n], amax_accumulate=True, want_q=False,
+                                want_q_t=False)
+            m.fp8_scale_update(m.FP8_SCALE_FROM_AMAX, amax=amax[n], scale=sc[n],
+                               scale_inv=si[n], clear_amax=True)
+            m.fp8_quantize_amax(src[n], scale_inv=si[n], q=q[n], want_q_t=False,
+                                want_amax=False)
+        m.fp8_linear_fwd(q["x"], q["w"], sc["x"], sc["w"], y=y)
+
+    def per_call_us(fn):
+        for _ in range(20):
+            fn()
+        out = []
+        for _ in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3 / iters)
+        return float(np.median(out))
+
+    eager_us = per_call_us(forward)
+    ref = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        forward()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        forward()
+    y.zero_()
+    graph.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    same = bool(torch.equal(y.view(torch.int16), ref.view(torch.int16)))
+    graph_us = per_call_us(graph.replay)
+    flops = 2.0 * 64 * 128 * 128
+    return {"workload": "one fp8 linear forward, current tensorwise scaling, x [64,128], "
+                        "W [128,128] N(0,1): amax pass, scale, cast for x and W, then the GEMM",
+            "launches": 7, "us_per_forward_eager": round(eager_us, 2),
+            "us_per_forward_hip_graph": round(graph_us, 2),
+            "graph_matches_eager": same,
+            "gflops_hip_graph": round(flops / (graph_us * 1e-6) / 1e9, 2)}
+
+
+def measure_config2(torch, m, repeats=5):
+    """Config 2: fp8 linear fwd + dgrad + wgrad at M = K = N = 4096 for 32 steps of delayed
+    scaling (16-step weight amax ring, one-step-delayed activation and gradient scales):
+    x ~ N(0,1) and g ~ N(0,1e-3) fresh every step, W ~ N(0,0.02) drifting by N(0,1e-4) per
+    step; every step's tensors are resident in HBM before timing (drawn on the device).
+    Each repeat runs the 32 steps from a fresh schedule; the median repeat is reported."""
+    M = K = N = 4096
+    steps = 32
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(2)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    xs = [torch.randn(M, K, device=dev, generator=gen).to(torch.bfloat16) for _ in range(steps)]
+    gs = [(torch.randn(M, N, device=dev, generator=gen) * 1e-3).to(torch.bfloat16)
+          for _ in range(steps)]
+    ws = [(torch.randn(N, K, device=dev, generator=gen) * 0.02).to(torch.bfloat16)]
+    for _ in range(steps - 1):
+        ws.append((ws[-1].float() + torch.randn(N, K, device=dev, generator=gen) * 1e-4)
+                  .to(torch.bfloat16))
+    bufs = dict(qw=torch.empty((N, K), **u8), qw_t=torch.empty((K, N), **u8),
+                qx=torch.empty((M, K), **u8), qx_t=torch.empty((K, M), **u8),
+                qg=torch.empty((M, N), **u8), qg_t=torch.empty((N, M), **u8))
+    y, dx, dw = (torch.empty((M, N), **bf), torch.empty((M, K), **bf),
+                 torch.empty((N, K), **bf))
+
+    def run(lin):
+        for t in range(steps):
+            lin.begin_step()
+            lin.forward(xs[t], ws[t], out=y, bufs=bufs)
+            lin.backward(gs[t], dx=dx, dw=dw, bufs=bufs)
+            lin.end_step()
+
+    run(m.DelayedScalingLinear(dev))                      # warm-up
+    times = []
+    for _ in range(repeats):
+        lin = m.DelayedScalingLinear(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        run(lin)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    flops = steps * 6.0 * M * N * K
+    return {"workload": "fp8 linear fwd+dgrad+wgrad, M=K=N=4096, 32 steps of delayed scaling, "
+                        "x N(0,1), W N(0,0.02) drifting N(0,1e-4), g N(0,1e-3)",
+            "steps": steps, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "ms_per_32_steps": round(ms, 4), "ms_per_step": round(ms / steps, 4),
+            "repeats": repeats}
 
 
 def measure_block_recipe(torch, m, workloads, steps, warmup):
@@ -527,24 +664,27 @@ def main():
         step()
 
     def timed_steps(layers=lins, steps=args.steps):
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
+        """(median ms per step, mean ms per step, wall seconds): an event at every step
+        boundary (none between the kernels of a step)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        start.record()
-        for _ in range(steps):
+        ev[0].record()
+        for i in range(steps):
             step(layers)
-        stop.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return start.elapsed_time(stop) / steps, time.perf_counter() - t0
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return float(np.median(per)), ev[0].elapsed_time(ev[-1]) / steps, \
+            time.perf_counter() - t0
 
-    # the timed region: K steps with nothing recorded between the kernels
-    ms_step, wall_s = timed_steps()
+    # the timed region: K steps with nothing recorded between the kernels of a step
+    ms_step, ms_step_mean, wall_s = timed_steps()
     # the same K steps again with a pair of HIP events around every kernel call (on the
     # launch stream): the per-launch durations of the roofline figures. Each event record
     # costs the stream a few microseconds, so this pass is slower as a whole.
     probe.active = True
-    ms_step_instr, _ = timed_steps()
+    ms_step_instr, _, _ = timed_steps()
     probe.active = False
     flops_step = 3 * 6.0 * M * N * K
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -569,6 +709,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_mean": round(ms_step_mean, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -611,7 +752,7 @@ def main():
         hsteps = max(3, args.steps // 3)
         for _ in range(2):
             step(hyb)
-        ms_h, _ = timed_steps(hyb, hsteps)
+        ms_h, _, _ = timed_steps(hyb, hsteps)
         hprobe.active = True
         timed_steps(hyb, hsteps)
         hprobe.active = False
@@ -632,6 +773,8 @@ def main():
     if not args.headline_only:
         torch.cuda.empty_cache()
         line["other_rows"] = {
+            "config1_current_scaling": measure_config1(torch, m, workloads),
+            "config2_delayed_4096": measure_config2(torch, m),
             "block_recipe": measure_block_recipe(torch, m, workloads, max(3, args.steps // 3), 2),
             "packed_varlen_padding": measure_varlen(torch, m, workloads, max(3, args.steps // 3), 2),
             "autograd_bias_f1": measure_f1(torch, m, max(3, args.steps // 3), 2),

@@ -68,3 +68,22 @@ def test_traffic_file_names_existing_sources():
     for files in srcs:
         for f in files:
             assert os.path.exists(os.path.join(root, f)), f
+
+
+def test_cpu_baseline_slab_quantize_is_the_oracle():
+    """The baseline's quantize in row slabs on threads gives the oracle's codes and transposed
+    codes byte for byte (slabs of unequal size included)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import workloads
+    from oracle.quantize import amax, quantize_tensorwise
+    from oracle.scaling import scale_from_amax
+    x = workloads.bf16_tensor("student_t", (100, 48), 3, 99, 0, nu=3)
+    _, si = scale_from_amax(amax(x))
+    q, q_t, _ = quantize_tensorwise(x, si)
+    with ThreadPoolExecutor(3) as pool:
+        for slabs in (1, 3, 7):
+            sq, sq_t = bench._oracle_quantize_slabs(x, si, pool, slabs)
+            assert np.array_equal(sq, q) and np.array_equal(sq_t, q_t), slabs
