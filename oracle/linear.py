@@ -24,7 +24,7 @@ from . import block as blk
 from .gemm import scaled_gemm
 from .quantize import amax as amax_of
 from .quantize import quantize_tensorwise
-from .scaling import E4M3_MAX, E5M2_MAX, StepCounter, WeightMeta, scale_from_amax
+from .scaling import E4M3_MAX, E5M2_MAX, WeightScales, refresh_due, scale_from_amax
 
 
 class DelayedLinear:
@@ -37,8 +37,9 @@ class DelayedLinear:
     def __init__(self, update_interval: int = 16, grad_format: str = "e4m3"):
         assert grad_format in ("e4m3", "e5m2")
         self.grad_format = grad_format
-        self.counter = StepCounter(update_interval)
-        self.w = WeightMeta(update_interval)
+        self.update_interval = update_interval
+        self.step = 0
+        self.w = WeightScales(update_interval)
         self.x_scale = np.float32(1.0)
         self.x_scale_inv = np.float32(1.0)
         self.g_scale = np.float32(1.0)
@@ -47,7 +48,8 @@ class DelayedLinear:
 
     def begin_step(self) -> bool:
         """``fp8_autocast`` entry: returns True if the weight scale refreshed."""
-        refreshed = self.counter.step()
+        self.step += 1
+        refreshed = refresh_due(self.step, self.update_interval)
         if refreshed:
             self.w.refresh()
         return refreshed
@@ -101,8 +103,8 @@ class DelayedLinear:
         return used
 
     def state(self) -> dict:
-        return dict(step=self.counter.step_count, w_scale=self.w.scale,
-                    w_scale_inv=self.w.scale_inv, hist=self.w.hist.copy(), idx=self.w.idx,
+        return dict(step=self.step, w_scale=self.w.scale,
+                    w_scale_inv=self.w.scale_inv, hist=self.w.hist, idx=self.w.pos,
                     x_scale=self.x_scale, x_scale_inv=self.x_scale_inv,
                     g_scale=self.g_scale, g_scale_inv=self.g_scale_inv)
 

@@ -1,19 +1,20 @@
-"""Scale arithmetic and the weight amax-history ring (test infrastructure only).
+"""Scale arithmetic and the weight amax window (test infrastructure only).
 
-Source: AstrAI ``astrai/extension/fp8_state.py``.
+Source: AstrAI ``astrai/extension/fp8_state.py`` (``_update_delayed_scale``,
+``FP8TensorMeta``, ``FP8State``, ``fp8_autocast``). What the schedule is, in
+its own terms:
 
-* ``_update_delayed_scale``: ``a = clamp_min(float32(amax), 1e-12)``,
-  ``scale = a / 448``, ``scale_inv = 448 / a``; written for the *next* call
-  (activations and gradients are scaled one step late).
-* ``FP8TensorMeta.__init__``: ``scale``, ``scale_inv`` start at 1.0; the amax
-  history has ``update_interval`` (16) entries, all initialised to **1.0**;
-  the ring index starts at 0.
-* ``FP8TensorMeta.record``: ``hist[idx] = amax``; ``idx = (idx + 1) % len``.
-* ``FP8TensorMeta.refresh``: ``m = max(hist)``; only if ``m > 0``:
-  ``scale = m / 448``, ``scale_inv = 448 / m``.
-* ``FP8State.step``: ``step_count += 1``; when ``step_count % 16 == 0`` every
-  weight meta refreshes. ``fp8_autocast`` calls ``step`` once per entry, i.e.
-  once per training step, before the forward.
+* a scale pair from one amax: ``a = max(amax, 1e-12)``, dequant scale
+  ``a / 448`` and quantize multiplier ``448 / a``; activations and gradients
+  take the pair of their previous step's amax (one step late);
+* every weight keeps a window of its last 16 recorded amaxes; before any is
+  recorded all 16 entries are 1.0. Each step records the amax of the weight
+  it quantized, the i-th recorded amax (counting from 0) taking entry
+  ``i mod 16``;
+* the weight's scale pair starts at (1.0, 1.0) and is recomputed from the
+  window's maximum m at the start of every step whose number (from 1) is a
+  multiple of 16, before that step's forward; when m is not positive (or is
+  NaN) the pair stays as it was.
 
 Readings (the pages leave the rounding open):
 
@@ -22,7 +23,7 @@ Readings (the pages leave the rounding open):
   followed by a multiply; the plain mathematical reading of the printed
   expression, one division, is used instead;
 * the clamp keeps NaN (``clamp_min`` propagates NaN), so a NaN amax gives NaN
-  scales; ``refresh`` skips a NaN window maximum because ``NaN > 0`` is false;
+  scales; a NaN window maximum leaves the weight's pair unchanged;
 * 1e-12 is the float32 nearest to 1e-12 (bits 0x2B8CBCCC), as a Python float
   scalar meets a float32 tensor in ``clamp_min``.
 """
@@ -49,34 +50,52 @@ def scale_from_amax(amax, fmax=E4M3_MAX) -> tuple[np.float32, np.float32]:
     return scale, scale_inv
 
 
-class WeightMeta:
-    """The weight half of ``FP8TensorMeta``: scale, scale_inv and the ring."""
+def window_after(recorded, length: int = UPDATE_INTERVAL) -> np.ndarray:
+    """The amax window after ``recorded`` (in order): ``length`` entries that start at 1.0,
+    the i-th recorded amax (from 0) in entry ``i mod length``."""
+    w = np.ones(length, dtype=np.float32)
+    for i, a in enumerate(recorded):
+        w[i % length] = np.float32(a)
+    return w
 
-    def __init__(self, update_interval: int = UPDATE_INTERVAL):
+
+def window_scale(window, fmax=E4M3_MAX):
+    """The scale pair from a window's maximum m, or None when m is NaN or not positive (the
+    weight then keeps the pair it had)."""
+    m = np.float32(np.max(np.asarray(window, dtype=np.float32)))   # NaN propagates
+    if not m > 0:
+        return None
+    fmax = np.float32(fmax)
+    return np.float32(m / fmax), np.float32(fmax / m)
+
+
+def refresh_due(step: int, interval: int = UPDATE_INTERVAL) -> bool:
+    """Whether step ``step`` (numbered from 1) recomputes the weight scales first."""
+    return step % interval == 0
+
+
+class WeightScales:
+    """A weight's scale pair and the amaxes recorded for it."""
+
+    def __init__(self, length: int = UPDATE_INTERVAL):
+        self.length = length
         self.scale = np.float32(1.0)
         self.scale_inv = np.float32(1.0)
-        self.hist = np.ones(update_interval, dtype=np.float32)
-        self.idx = 0
+        self.recorded = []
+
+    @property
+    def hist(self) -> np.ndarray:
+        return window_after(self.recorded, self.length)
+
+    @property
+    def pos(self) -> int:
+        """The window entry the next recorded amax goes to."""
+        return len(self.recorded) % self.length
 
     def record(self, amax) -> None:
-        self.hist[self.idx] = np.float32(amax)
-        self.idx = (self.idx + 1) % self.hist.size
+        self.recorded.append(np.float32(amax))
 
     def refresh(self) -> None:
-        m = np.float32(np.max(self.hist))       # NaN propagates through max
-        if m > 0:                                # False for NaN: keep the old scale
-            self.scale = np.float32(m / E4M3_MAX)
-            self.scale_inv = np.float32(E4M3_MAX / m)
-
-
-class StepCounter:
-    """``FP8State.step``: one advance per training step."""
-
-    def __init__(self, update_interval: int = UPDATE_INTERVAL):
-        self.update_interval = update_interval
-        self.step_count = 0
-
-    def step(self) -> bool:
-        """Advance; return True when the weight metas must refresh now."""
-        self.step_count += 1
-        return self.step_count % self.update_interval == 0
+        pair = window_scale(self.hist)
+        if pair is not None:
+            self.scale, self.scale_inv = pair

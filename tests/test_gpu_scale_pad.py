@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 from oracle.padding import pad_rows, padded_count
-from oracle.scaling import WeightMeta, scale_from_amax
+from oracle.scaling import WeightScales, scale_from_amax
 from tests.gpu_util import dev_f32, f32_bits, host_bf16_bits, note
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,7 @@ def test_record_and_refresh_ring(lib):
     """The hand-worked 'inc' schedule: a_t = t/64 recorded for 48 steps, refresh every 16."""
     hist = torch.ones(16, device="cuda")
     scale, scale_inv = dev_f32([1.0]), dev_f32([1.0])
-    ref = WeightMeta()
+    ref = WeightScales()
     for t in range(1, 49):
         if t % 16 == 0:
             note(f"REFRESH at step {t}")
@@ -62,7 +62,7 @@ def test_record_and_refresh_ring(lib):
         assert f32_bits(scale.item()) == f32_bits(ref.scale), t
         assert f32_bits(scale_inv.item()) == f32_bits(ref.scale_inv), t
         a = dev_f32([t / 64])
-        lib.fp8_scale_update(lib.FP8_SCALE_RECORD, amax=a, hist=hist, pos=ref.idx)
+        lib.fp8_scale_update(lib.FP8_SCALE_RECORD, amax=a, hist=hist, pos=ref.pos)
         ref.record(np.float32(t / 64))
     torch.cuda.synchronize()
     assert np.array_equal(hist.cpu().numpy(), ref.hist)

@@ -110,15 +110,29 @@ def test_weight_ring_matches_hand_schedule(golden_dir):
             lin.begin_step()
             assert (lin.w.scale, lin.w.scale_inv) == expect[t], (name, t)
             lin.w.record(np.float32(float(amax_of(t))))
-            assert lin.w.idx == t % 16
+            assert lin.w.pos == t % 16
 
 
 def test_ring_nan_window_keeps_scale():
-    m = scaling.WeightMeta()
+    m = scaling.WeightScales()
     m.scale, m.scale_inv = np.float32(0.5), np.float32(2.0)
     m.record(np.float32(np.nan))
     m.refresh()
     assert m.scale == np.float32(0.5) and m.scale_inv == np.float32(2.0)
+
+
+def test_window_and_refresh_predicate():
+    """The window as a function of what was recorded: ones at first, entry i mod 16 for the
+    i-th amax (17 records wrap to entry 0); refreshes fall on steps 16, 32, ..."""
+    w = scaling.window_after([])
+    assert w.dtype == np.float32 and np.all(w == 1.0) and w.size == 16
+    w = scaling.window_after([np.float32(v) for v in range(2, 19)])   # 17 amaxes: 2 .. 18
+    assert w[0] == 18 and w[1] == 3 and w[15] == 17
+    assert [t for t in range(1, 50) if scaling.refresh_due(t)] == [16, 32, 48]
+    assert scaling.window_scale(np.zeros(16, np.float32)) is None
+    assert scaling.window_scale(np.full(16, np.nan, np.float32)) is None
+    s, si = scaling.window_scale(np.float32([0.5] * 15 + [448.0]))
+    assert s == np.float32(1.0) and si == np.float32(1.0)
 
 
 def test_activation_and_grad_scales_are_one_step_late():
