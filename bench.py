@@ -265,6 +265,20 @@ def cpu_baseline(sample_tokens: int) -> dict:
                        + ("" if S == M else f", scaled x{M / S:g} to the full step"))}
 
 
+def _time_steps(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def measure_config1(torch, m, workloads, iters=200, repeats=7):
     """Config 1: one fp8 linear forward with current tensorwise scaling, x [64, 128],
     W [128, 128], N(0, 1): for each operand an amax pass, the scale from that amax (no
@@ -387,6 +401,58 @@ def measure_config2(torch, m, repeats=5):
             "steps": steps, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "ms_per_32_steps": round(ms, 4), "ms_per_step": round(ms / steps, 4),
             "repeats": repeats}
+
+
+def measure_quantize_vs_copy(torch, m, reps=5):
+    """The quantize pass on every tensor shape of the step (and the packed varlen batch),
+    beside a copy of the same bytes at the same access width: the library's padding kernel
+    copying the bf16 tensor into a second buffer (2 B read and 2 B written per element,
+    16-byte loads and stores), which is the rate an HBM stream of this mix reaches on the
+    box. Buffers rotate through enough sets (at least 1.5 GB) that no launch finds its
+    data in the 256 MB Infinity Cache."""
+    import math
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(7)
+    out = {}
+    for name, (rows, cols) in (("x", (8192, 4096)), ("w_gate_up", (14336, 4096)),
+                               ("w_down", (4096, 14336)), ("g_gate_up_and_h", (8192, 14336)),
+                               ("varlen_54672", (54672, 4096))):
+        per_set = 4 * rows * cols
+        sets = max(2, math.ceil(1.5e9 / per_set))
+        xs = [torch.randn(rows, cols, device=dev, generator=gen).to(torch.bfloat16)
+              for _ in range(sets)]
+        si = torch.full((1,), 64.0, device=dev)
+        amax = torch.zeros(1, device=dev)
+        qs = [torch.empty((rows, cols), dtype=torch.uint8, device=dev) for _ in range(sets)]
+        qts = [torch.empty((cols, rows), dtype=torch.uint8, device=dev) for _ in range(sets)]
+        ds = [torch.empty_like(t) for t in xs]
+
+        def timed(fn):
+            for i in range(sets):
+                fn(i)
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(3):
+                    for i in range(sets):
+                        fn(i)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / (3 * sets))
+            return float(np.median(ts))
+
+        q_us = timed(lambda i: m.fp8_quantize_amax(xs[i], scale_inv=si, q=qs[i], q_t=qts[i],
+                                                   amax=amax, amax_accumulate=True))
+        c_us = timed(lambda i: m.fp8_pad_tokens(xs[i], x_pad=ds[i]))
+        out[name] = {"shape": [rows, cols], "quantize_us": round(q_us, 2),
+                     "quantize_tbs": round(per_set / q_us / 1e6, 3),
+                     "copy_us": round(c_us, 2), "copy_tbs": round(per_set / c_us / 1e6, 3),
+                     "quantize_over_copy": round(c_us / q_us, 3)}
+        del xs, qs, qts, ds
+        torch.cuda.empty_cache()
+    return out
 
 
 def measure_block_recipe(torch, m, workloads, steps, warmup):
@@ -775,6 +841,7 @@ def main():
         line["other_rows"] = {
             "config1_current_scaling": measure_config1(torch, m, workloads),
             "config2_delayed_4096": measure_config2(torch, m),
+            "quantize_vs_copy": measure_quantize_vs_copy(torch, m),
             "block_recipe": measure_block_recipe(torch, m, workloads, max(3, args.steps // 3), 2),
             "packed_varlen_padding": measure_varlen(torch, m, workloads, max(3, args.steps // 3), 2),
             "autograd_bias_f1": measure_f1(torch, m, max(3, args.steps // 3), 2),

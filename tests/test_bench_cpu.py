@@ -87,3 +87,36 @@ def test_cpu_baseline_slab_quantize_is_the_oracle():
         for slabs in (1, 3, 7):
             sq, sq_t = bench._oracle_quantize_slabs(x, si, pool, slabs)
             assert np.array_equal(sq, q) and np.array_equal(sq_t, q_t), slabs
+
+
+def test_bench_functions_name_only_defined_names():
+    """Every bare name a function of bench.py reads is bound somewhere it can see: its own
+    parameters and assignments, an enclosing function's, the module's, or a builtin (the GPU
+    paths of bench.py cannot run here, so a missing helper would only show on the GPU)."""
+    import ast
+    import builtins
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+
+    def bound(node):
+        names = set()
+        for n in ast.walk(node):
+            if isinstance(n, ast.Name) and isinstance(n.ctx, (ast.Store, ast.Del)):
+                names.add(n.id)
+            elif isinstance(n, (ast.FunctionDef, ast.ClassDef)):
+                names.add(n.name)
+            elif isinstance(n, (ast.Import, ast.ImportFrom)):
+                names.update((a.asname or a.name).split(".")[0] for a in n.names)
+            elif isinstance(n, ast.arg):
+                names.add(n.arg)
+            elif isinstance(n, ast.ExceptHandler) and n.name:
+                names.add(n.name)
+        return names
+
+    module_names = bound(tree) | set(dir(builtins))
+    missing = []
+    for fn in [n for n in ast.walk(tree) if isinstance(n, ast.FunctionDef)]:
+        visible = module_names | bound(fn)
+        for n in ast.walk(fn):
+            if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Load) and n.id not in visible:
+                missing.append((fn.name, n.id, n.lineno))
+    assert not missing, missing
