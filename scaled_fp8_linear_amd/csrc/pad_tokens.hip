@@ -1,8 +1,10 @@
 // Token-count padding of a packed batch (NeMo PR 15754 review thread:
 // pad = (-T) % seq_multiple; SpecForge PR 2, Constraints: FP8 GEMMs need the
 // token count to be a multiple of 16). Rows [0, T) are copied (unless the
-// copy is in place) and rows [T, T_pad) are zeroed. Pure HBM copy: 16-byte
-// vector loads and stores, a grid-stride loop over 16-byte units.
+// copy is in place) and rows [T, T_pad) are zeroed. Pure HBM copy: a 1024-lane
+// workgroup moves 8 x 16 KB, each lane eight 16-byte units (all loads issued,
+// streaming, before the first store), which keeps more bytes in flight per CU
+// than a grid-stride loop with one load per lane.
 #include "common.h"
 #include "launch.h"
 
@@ -10,12 +12,22 @@ namespace fp8lin {
 
 namespace {
 
-__global__ void __launch_bounds__(256)
+constexpr int kPadLanes = 1024, kPadUnits = 8;   // 16-byte units per lane
+
+__global__ void __launch_bounds__(kPadLanes)
 pad_rows_kernel(const uint4* __restrict__ src, int64_t n_copy, uint4* __restrict__ dst,
                 int64_t n_total) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_total; i += stride) {
-    dst[i] = (i < n_copy) ? src[i] : make_uint4(0, 0, 0, 0);
+  const int64_t base = (int64_t)blockIdx.x * (kPadLanes * kPadUnits) + threadIdx.x;
+  uint4 v[kPadUnits];
+#pragma unroll
+  for (int j = 0; j < kPadUnits; ++j) {
+    const int64_t i = base + (int64_t)kPadLanes * j;
+    v[j] = i < n_copy ? ld_stream16(src + i) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kPadUnits; ++j) {
+    const int64_t i = base + (int64_t)kPadLanes * j;
+    if (i < n_total) dst[i] = v[j];
   }
 }
 
@@ -41,14 +53,16 @@ hipError_t launch_pad_tokens(const uint16_t* x, int64_t T, int64_t cols, int64_t
   uint16_t* dst = x_pad + first;
   const bool vec = ((first % 8) == 0) && ((n_copy % 8) == 0) && ((n_total % 8) == 0) &&
                    ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 == 0);
-  const int64_t units = vec ? n_total / 8 : n_total;
-  int64_t blocks = (units + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
   if (vec) {
-    hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+    const int64_t units = n_total / 8;
+    const int64_t blocks = (units + kPadLanes * kPadUnits - 1) / (kPadLanes * kPadUnits);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)blocks), dim3(kPadLanes), 0, s,
                        reinterpret_cast<const uint4*>(src), n_copy / 8,
-                       reinterpret_cast<uint4*>(dst), n_total / 8);
+                       reinterpret_cast<uint4*>(dst), units);
   } else {
+    int64_t blocks = (n_total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(pad_rows_bytes_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, n_copy,
                        dst, n_total);
   }
