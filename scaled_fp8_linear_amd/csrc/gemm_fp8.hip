@@ -547,7 +547,9 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   const int wm = wave / C::WN, wn = wave % C::WN;
   const v4i rsA = make_rsrc(A, (uint32_t)(M * K));
   const v4i rsB = make_rsrc(B, (uint32_t)(N * K));
-  const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc(D, 0, M * N * 2, kRsrcWord3);
+  // D as a raw buffer over the valid rows: stores to rows at or past M_valid are dropped
+  const __amdgpu_buffer_rsrc_t rsD =
+      __builtin_amdgcn_make_buffer_rsrc(D, 0, M_valid * N * 2, kRsrcWord3);
   const float scl = __builtin_bit_cast(
       float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sa[0] * sb[0])));
 
@@ -640,39 +642,144 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   const int ns = max(4, (((K + kStageK - 1) / kStageK) + 1) & ~1);
   Rows cur = rows_of(0), nxt = rows_of(1);
 
+  // ---- epilogue pieces: scale, round to bf16, 16-byte stores. Store op o of row i of the
+  // wave's 16x16 tiles: for o < kPairs the tiles j = 2 o, 2 o + 1 (after v_permlane16_swap
+  // lane group g = l / 16 holds 8 consecutive n, columns 8 (g / 2) .. + 8 of tile j + g % 2);
+  // with an odd CT, op kPairs is the last tile alone, 8 bytes (4 consecutive n) per lane.
+  // Rows at or past M_valid lie past the end of D's buffer range (rsD covers the valid rows
+  // only) and are dropped there; the launcher writes their zeros.
+  constexpr int kPairs = CT / 2, kOps = kPairs + CT % 2;   // store ops per row
+  static_assert(kStores == RT * kOps, "store count");
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  // BIAS: tile j's 4 columns of the lane are n0 + wn WTN + 16 j + 4 g .. + 3 (packed bf16;
+  // columns past N read as 0)
+  uint2 bj[BIAS ? CT : 1];
+  auto load_bias = [&](int n0) {
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        const int n = n0 + wn * C::WTN + 16 * j + 4 * g4;
+        bj[j] = n < N ? *reinterpret_cast<const uint2*>(bias + n) : make_uint2(0u, 0u);
+      }
+    }
+  };
+  // the packed output of op o of row i (BIAS: the float32 bias added after the scale,
+  // before the one rounding)
+  auto op_value = [&](int i, int o) -> v4i {
+    const float si = scl;
+    auto val = [&](int j, int r) {
+      if constexpr (BIAS) {
+        const uint32_t w = r < 2 ? bj[j].x : bj[j].y;
+        return acc[i][j][r] * si + __uint_as_float(r % 2 ? (w & 0xFFFF0000u) : (w << 16));
+      } else {
+        return acc[i][j][r] * si;
+      }
+    };
+    if (o < kPairs) {
+      const int j = 2 * o;
+      const uint32_t p0j = pack_bf16x2(val(j, 0), val(j, 1));
+      const uint32_t p1j = pack_bf16x2(val(j, 2), val(j, 3));
+      const uint32_t p0k = pack_bf16x2(val(j + 1, 0), val(j + 1, 1));
+      const uint32_t p1k = pack_bf16x2(val(j + 1, 2), val(j + 1, 3));
+      const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
+      const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
+      return v4i{(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
+    }
+    constexpr int j = CT - 1;
+    return v4i{(int)pack_bf16x2(val(j, 0), val(j, 1)), (int)pack_bf16x2(val(j, 2), val(j, 3)),
+               0, 0};
+  };
+  // the lane's part of its output offsets (bytes): its row in the workgroup tile times N
+  // plus its first column in the op; an op adds the tile origin, its 16 i rows and 32 o
+  // columns, all wave-uniform. The launcher keeps every row below M + BM + 1 inside 2^31
+  // bytes, so a row at or past M_valid lands at or past the end of rsD's range, where the
+  // store is dropped; a column past N would land in the next row, so such a piece gets an
+  // offset past the end.
+  const int lcol_p = wn * C::WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
+  const int lcol_s = wn * C::WTN + 16 * (CT - 1) + 4 * g4;
+  const uint32_t lrow_off = (uint32_t)(wm * C::WTM + r16) * (uint32_t)N * 2u;
+  const uint32_t loff_p = lrow_off + 2u * (uint32_t)lcol_p;
+  const uint32_t loff_s = lrow_off + 2u * (uint32_t)lcol_s;
+  auto op_store = [&](int i, int o, v4i v, int m0, int n0) {
+    const uint32_t base = ((uint32_t)(m0 + 16 * i) * (uint32_t)N + (uint32_t)n0) * 2u;
+    if (o < kPairs) {
+      const bool in = lcol_p < N - n0 - 32 * o;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rsD, in ? base + 64u * o + loff_p : kOutOfRange,
+                                             0, 0);
+    } else {
+      const bool in = lcol_s < N - n0;
+      __builtin_amdgcn_raw_buffer_store_b64(v2i{v[0], v[1]}, rsD, in ? base + loff_s : kOutOfRange,
+                                            0, 0);
+    }
+  };
+
   // One stage. Bc and Alo[0]: this stage's B fragments and A row 0 (read before); Bn and
   // Alo[0]: the next stage's, read in the second half.
-  // FIRST: the tile's first stage (sums start at zero; after a previous tile, that
-  // tile's kStores stores are the newest memory operations, issued after the loads this
-  // stage waits for: loads and stores retire in order, so they may stay in flight).
-  // LAST: the tile's last stage, which reads no fragments of the next stage (they are
-  // read after the epilogue, so that they hold no registers through it).
-  auto stage = [&](auto FIRST_, auto LAST_, int s, uint8_t* mine, uint8_t* other, v8i* Bc,
-                   v8i* Bn, bool after) {
+  // FIRST: the tile's first stage (sums start at zero). LAST: the tile's last stage, which
+  // reads no fragments of the next stage (they are read after it, so that they hold no
+  // registers through it).
+  // The epilogue of a tile runs in the shadow of the matrix cores, in two halves:
+  // EPI = 1 (the LAST stage): after the first half, rows 0 .. RH-1 are final; their store
+  //   ops run during the second half. All loads of that half (the next tile's stage 1) go
+  //   out first, one per MFMA, and the ops (value and store) are spread over the MFMAs
+  //   left, so exactly kStores stores follow those loads.
+  // EPI = 2 (a FIRST stage after a tile): the first half's MFMAs write rows 0 .. RH-1 only,
+  //   so the previous tile's rows RH .. RT-1 (at em0, en0) go out in between. The wait in
+  //   the middle of the stage then lets those kStores stores stay in flight: loads and
+  //   stores retire in order, and the stage-1 loads it waits for were issued before them.
+  auto stage = [&](auto FIRST_, auto LAST_, auto EPI_, int s, uint8_t* mine, uint8_t* other,
+                   v8i* Bc, v8i* Bn, int em0, int en0) {
     constexpr bool FIRST = decltype(FIRST_)::value != 0, LAST = decltype(LAST_)::value != 0;
+    constexpr int EPI = decltype(EPI_)::value;
+    static_assert(EPI != 1 || LAST, "the first epilogue half runs in a last stage");
+    static_assert(EPI != 2 || FIRST, "the second epilogue half runs in a first stage");
     const v4f z = {};
     // first half: rows 0 .. RH-1; A rows 1 .. RT-1 are read in between (row i is first
     // needed by MFMA i CT, and is read among the first ones)
+    if constexpr (LAST) load_bias(en0);
 #pragma unroll
     for (int i = 1; i < RH; ++i) Alo[i] = rdA(mine, i);
 #pragma unroll
     for (int i = 0; i < RS; ++i) Ahi[i] = rdA(mine, RH + i);
+    if constexpr (EPI == 2) {
+      // RS kOps ops of the previous tile spread over the RH CT MFMAs, in a pinned order
+      constexpr int kMf = RH * CT, kEp = RS * kOps;
 #pragma unroll
-    for (int i = 0; i < RH; ++i)
-#pragma unroll
-      for (int j = 0; j < CT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Alo[i],
-                                                                     FIRST ? z : acc[i][j], 0,
+      for (int x = 0; x < kMf; ++x) {
+        const int i = x / CT, j = x % CT;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Alo[i], z, 0,
                                                                      C::AFMT, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (em0 < M) {             // false before the first tile: nothing to store
 #pragma unroll
-    for (int x = 0; x < RH * CT; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (x % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int k = x * kEp / kMf; k < (x + 1) * kEp / kMf; ++k)
+            op_store(RH + k / kOps, k % kOps, op_value(RH + k / kOps, k % kOps), em0, en0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RH; ++i)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Alo[i],
+                                                                       FIRST ? z : acc[i][j], 0,
+                                                                       C::AFMT, 0, 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < RH * CT; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (x % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // stage s + 1 landed (own loads), own LDS reads done; then for every wave
-    if (FIRST && after) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStores) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // stage s + 1 landed (own loads), own LDS reads done; then for every wave. In the first
+    // tile no stores follow the stage-1 loads.
+    if constexpr (EPI == 2) {
+      if (em0 >= M) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStores) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // second half: rows RH .. RT-1, with the loads of stage s + 2 (into `mine`) and the
@@ -682,6 +789,8 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     const int kb = gs < ns ? gs : gs - ns;
     constexpr int kSecond = RS * CT;                 // MFMAs in the second half
     constexpr int kReads = CT + 1;                   // fragments to read
+    constexpr int kEpLo = RH * kOps;                 // EPI = 1: store ops of rows 0 .. RH-1
+    static_assert(EPI != 1 || kDma < kSecond, "the loads go out before the stores");
 #pragma unroll
     for (int x = 0; x < kSecond; ++x) {
       const int i = RH + x / CT, j = x % CT;
@@ -689,78 +798,20 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
                                                                    FIRST ? z : acc[i][j], 0,
                                                                    C::AFMT, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (x * kDma / kSecond != (x + 1) * kDma / kSecond) dma(x * kDma / kSecond, mine, r, kb);
-      if (!LAST && x * kReads / kSecond != (x + 1) * kReads / kSecond) {
-        const int f = x * kReads / kSecond;
-        if (f < CT) Bn[f] = rdB(other, f);
-        else Alo[f - CT] = rdA(other, f - CT);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // epilogue: scale, round to bf16, 16-byte stores. Tiles j and j + 1 of a row go
-  // together: after v_permlane16_swap on their packed results, lane group g (= l / 16)
-  // holds 8 consecutive n, namely columns 8 (g / 2) .. + 8 of tile j + g % 2. One code
-  // path for every tile (a second one would have the compiler compute all 256 scaled
-  // values up front for both): rows at or past M_valid are replaced by zeros, pieces
-  // outside D get an offset past its end, which the range check drops.
-  // With an odd tile count per row, the last tile goes out on its own: 8 bytes (4
-  // consecutive n) per lane.
-  auto epilogue = [&](int m0, int n0) {
-    // BIAS: tile j's 4 columns of the lane are n0 + wn WTN + 16 j + 4 g .. + 3 (kept as
-    // packed bf16; columns past N read as 0)
-    uint2 bj[BIAS ? CT : 1];
-    if constexpr (BIAS) {
+      if constexpr (EPI == 1) {
+        // the loads first (one per MFMA), then the store ops spread over the MFMAs left
+        if (x < kDma) dma(x, mine, r, kb);
 #pragma unroll
-      for (int j = 0; j < CT; ++j) {
-        const int n = n0 + wn * C::WTN + 16 * j + 4 * g4;
-        bj[j] = n < N ? *reinterpret_cast<const uint2*>(bias + n) : make_uint2(0u, 0u);
-      }
-    }
-    const int mrow = m0 + wm * C::WTM + r16;
-    const int ncol = n0 + wn * C::WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
-    const uint32_t base = ((uint32_t)mrow * (uint32_t)N + (uint32_t)ncol) * 2u;
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int m = mrow + 16 * i;
-      const bool live = m < M_valid;   // rows past it are written as zeros, whatever
-                                       // their sums hold (a select, not a product)
-      const float si = scl;
-      // BIAS: the float32 bias of the lane's 4 columns of tile j, added after the scale
-      auto val = [&](int j, int r) {
-        if constexpr (BIAS) {
-          const uint32_t w = r < 2 ? bj[j].x : bj[j].y;
-          return acc[i][j][r] * si + __uint_as_float(r % 2 ? (w & 0xFFFF0000u) : (w << 16));
-        } else {
-          return acc[i][j][r] * si;
+        for (int k = 0; k < kEpLo; ++k)
+          if (kDma + k * (kSecond - kDma) / kEpLo == x)
+            op_store(k / kOps, k % kOps, op_value(k / kOps, k % kOps), em0, en0);
+      } else {
+        if (x * kDma / kSecond != (x + 1) * kDma / kSecond) dma(x * kDma / kSecond, mine, r, kb);
+        if (!LAST && x * kReads / kSecond != (x + 1) * kReads / kSecond) {
+          const int f = x * kReads / kSecond;
+          if (f < CT) Bn[f] = rdB(other, f);
+          else Alo[f - CT] = rdA(other, f - CT);
         }
-      };
-#pragma unroll
-      for (int jp = 0; jp < CT / 2; ++jp) {
-        const int j = 2 * jp;
-        const uint32_t p0j = pack_bf16x2(val(j, 0), val(j, 1));
-        const uint32_t p1j = pack_bf16x2(val(j, 2), val(j, 3));
-        const uint32_t p0k = pack_bf16x2(val(j + 1, 0), val(j + 1, 1));
-        const uint32_t p1k = pack_bf16x2(val(j + 1, 2), val(j + 1, 3));
-        const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
-        const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
-        v4i o = {(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
-        if (!live) o = v4i{0, 0, 0, 0};
-        const bool in = m < M && ncol + 32 * jp < N;
-        const uint32_t off =
-            in ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
-      }
-      if constexpr (CT % 2 != 0) {
-        constexpr int j = CT - 1;
-        typedef int v2i __attribute__((ext_vector_type(2)));
-        const int n = n0 + wn * C::WTN + 16 * j + 4 * g4;
-        v2i o = {(int)pack_bf16x2(val(j, 0), val(j, 1)), (int)pack_bf16x2(val(j, 2), val(j, 3))};
-        if (!live) o = v2i{0, 0};
-        const uint32_t off =
-            (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b64(o, rsD, off, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -780,23 +831,31 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     Alo[0] = rdA(slot0, 0);
   };
   first_frags();
+  // the previous tile (its rows RH .. RT-1 still to go); a row origin of M: none
+  int pm0 = M, pn0 = 0;
   for (int ti = 0; ti < count; ++ti) {
     int cm0, cn0;
     tile_mn(ti, cm0, cn0);
-    const bool after = ti > 0;
     // stages 0, 1 | 2 .. ns - 3 | ns - 2, ns - 1 (ns is even and at least 4)
-    stage(IC<1>{}, IC<0>{}, 0, slot0, slot1, Bf0, Bf1, after);
-    stage(IC<0>{}, IC<0>{}, 1, slot1, slot0, Bf1, Bf0, false);
+    stage(IC<1>{}, IC<0>{}, IC<2>{}, 0, slot0, slot1, Bf0, Bf1, pm0, pn0);
+    stage(IC<0>{}, IC<0>{}, IC<0>{}, 1, slot1, slot0, Bf1, Bf0, 0, 0);
     for (int s = 2; s < ns - 2; s += 2) {
-      stage(IC<0>{}, IC<0>{}, s, slot0, slot1, Bf0, Bf1, false);
-      stage(IC<0>{}, IC<0>{}, s + 1, slot1, slot0, Bf1, Bf0, false);
+      stage(IC<0>{}, IC<0>{}, IC<0>{}, s, slot0, slot1, Bf0, Bf1, 0, 0);
+      stage(IC<0>{}, IC<0>{}, IC<0>{}, s + 1, slot1, slot0, Bf1, Bf0, 0, 0);
     }
-    stage(IC<0>{}, IC<0>{}, ns - 2, slot0, slot1, Bf0, Bf1, false);
-    stage(IC<0>{}, IC<1>{}, ns - 1, slot1, slot0, Bf1, Bf0, false);
-    epilogue(cm0, cn0);
+    stage(IC<0>{}, IC<0>{}, IC<0>{}, ns - 2, slot0, slot1, Bf0, Bf1, 0, 0);
+    stage(IC<0>{}, IC<1>{}, IC<1>{}, ns - 1, slot1, slot0, Bf1, Bf0, cm0, cn0);
     first_frags();                     // the next tile's stage 0, published at stage ns - 1
+    pm0 = cm0;
+    pn0 = cn0;
     cur = nxt;
     nxt = rows_of(ti + 2);
+  }
+  if (count > 0) {
+    // the last tile's rows RH .. RT-1
+#pragma unroll
+    for (int k = 0; k < RS * kOps; ++k)
+      op_store(RH + k / kOps, k % kOps, op_value(RH + k / kOps, k % kOps), pm0, pn0);
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // no load may land after exit
 }
@@ -1307,6 +1366,13 @@ hipError_t run_mx16(const uint8_t* A, const uint8_t* B, const float* sa, const f
   if (grid == kMaxWorkgroups) xcd_split(tiles_m, tiles_n, C::BM, C::BN, split_m, split_n);
   const dim3 g((unsigned)grid), b(C::kThreads);
   const bool tail = K % (2 * kStageK) != 0;
+  // the kernel leaves rows at or past M_valid alone (they are past its output range):
+  // their zeros come from a fill kernel
+  if (M_valid < M) {
+    const hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(D + (int64_t)M_valid * N), 0u,
+                                         (int64_t)(M - M_valid) * N / 2, s);
+    if (e != hipSuccess) return e;
+  }
   if (bias == nullptr && !tail)
     hipLaunchKernelGGL((gemm_fp8_mx16_kernel<C, false, false>), g, b, 0, s, A, B, sa, sb, bias, D,
                        M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
@@ -1379,7 +1445,8 @@ template <int AF>
 hipError_t run_tensorwise_fmt(const uint8_t* A, const uint8_t* B, const float* sa,
                               const float* sb, const uint16_t* bias, uint16_t* D, int m, int n,
                               int k, int mv, hipStream_t s) {
-  const bool mx16_ok = k >= 4 * kStageK;
+  // the 16x16x128 kernel's output offsets are 32-bit for rows up to M + 257
+  const bool mx16_ok = k >= 4 * kStageK && ((int64_t)m + 257) * n * 2 < ((int64_t)1 << 31);
   const bool big = (int64_t)m * n >= (int64_t)2048 * 2048;
   if (big && mx16_ok) {
     // Beyond one round of 256x256 tiles, the tile shape with the shortest makespan:

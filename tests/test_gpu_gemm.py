@@ -262,15 +262,18 @@ def test_full_size_backward_shapes_sampled(lib, M, N, K, what):
         assert abs(yh[m, n] - D) <= bound, (what, m, n, yh[m, n], D, bound)
 
 
-@pytest.mark.parametrize("M,N,K,mv", [(2304, 2048, 512, 2200), (272, 256, 128, 200)])
+@pytest.mark.parametrize("M,N,K,mv", [(2304, 2048, 512, 2200), (2304, 2048, 512, 0),
+                                      (272, 256, 128, 200)])
 def test_padded_rows_are_zero_even_if_nan(lib, M, N, K, mv):
     """Rows at or past M_valid are written as zeros whatever their codes hold: here NaN
-    codes (0x7F), whose sums are NaN (both the 16x16x128 kernel's shape and a small one)."""
+    codes (0x7F), whose sums are NaN (both the 16x16x128 kernel's shape and a small one),
+    into an output that held NaN before the call."""
     qa, sa = _codes((M, K), 51 + M, "normal", std=1.0)
     qb, sb = _codes((N, K), 52 + N, "normal", std=1.0)
     qa[mv:] = 0x7F
     note(f"fp8_linear_fwd NaN pad rows M={M} N={N} K={K} M_valid={mv}")
-    y = lib.fp8_linear_fwd(_dev(qa), _dev(qb), dev_f32(sa), dev_f32(sb), M_valid=mv)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lib.fp8_linear_fwd(_dev(qa), _dev(qb), dev_f32(sa), dev_f32(sb), y=y, M_valid=mv)
     torch.cuda.synchronize()
     yh = host_bf16_f64(y)
     assert np.all(yh[mv:] == 0), "padded rows"
