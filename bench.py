@@ -49,6 +49,9 @@ def _parse():
                     help="only time one GEMM shape on random, constant and zero codes")
     ap.add_argument("--shape", default="8192,4096,14336",
                     help="M,N,K of the --data-sensitivity GEMM")
+    ap.add_argument("--profile-gemms", action="store_true",
+                    help="only run every GEMM launch shape of the step and of the block recipe "
+                         "(5 launches each after 2 warm-up launches), for counter collection")
     return ap.parse_args()
 
 
@@ -106,6 +109,65 @@ def data_sensitivity(launches=20, shape=(8192, 4096, 14336)):
         res[name] = {"us_per_launch": round(us, 1), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
         print(json.dumps({"data_sensitivity": name, **res[name]}), flush=True)
     print(json.dumps({"data_sensitivity": res, "shape": [M, N, K], "launches": launches}))
+
+
+def profile_gemms(launches=5, warmup=2):
+    """Every GEMM launch shape of the MLP step (tensorwise; the two 256x256-tile shapes and the
+    two wgrad shapes with 224-row / 224-column tiles) and the block recipe's forward, dgrad and
+    wgrad at M=16384, K=N=8192, on operand codes the library quantizes from N(0,1) data, with a
+    scale that keeps the codes spread over the format. One line per shape with the event time
+    per launch; meant to run under rocprofv3 counter collection."""
+    import torch
+    import scaled_fp8_linear_amd as m
+    m.load()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(3)
+
+    def codes(rows, cols):
+        x = torch.randn(rows, cols, device=dev, generator=gen).to(torch.bfloat16)
+        q = m.fp8_quantize_amax(x, scale_inv=torch.full((1,), 64.0, device=dev), want_q_t=False)[0]
+        return q
+
+    def timed(name, fn, flops):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(launches):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        print(json.dumps({"gemm": name, "us_per_launch": round(us, 1),
+                          "tflops": round(flops / us / 1e6, 1)}), flush=True)
+
+    one = torch.ones(1, device=dev)
+    for M, N, K in ((8192, 14336, 4096), (8192, 4096, 14336), (14336, 4096, 8192),
+                    (4096, 14336, 8192)):
+        qa, qb = codes(M, K), codes(N, K)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        timed(f"tensorwise {M}x{N}x{K}", lambda: m.fp8_linear_fwd(qa, qb, one, one, y=y),
+              2.0 * M * N * K)
+        del qa, qb, y
+    M, N, K = 16384, 8192, 8192
+    B = m.FP8_BLOCK_1x128
+    x = torch.randn(M, K, device=dev, generator=gen).to(torch.bfloat16)
+    w = torch.randn(N, K, device=dev, generator=gen).to(torch.bfloat16)
+    g = torch.randn(M, N, device=dev, generator=gen).to(torch.bfloat16)
+    qx, qx_t, _, sx, sx_t = m.fp8_quantize_amax(x, gran=B)
+    qw, qw_t, _, sw, sw_t = m.fp8_quantize_amax(w, gran=m.FP8_BLOCK_128x128)
+    qg, qg_t, _, sg, sg_t = m.fp8_quantize_amax(g, gran=B)
+    del x, w, g
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    f = 2.0 * M * N * K
+    timed("block fwd 16384x8192x8192", lambda: m.fp8_linear_fwd(qx, qw, sx, sw, y=y, gran=B), f)
+    timed("block dgrad 16384x8192x8192",
+          lambda: m.fp8_linear_dgrad(qg, qw_t, sg, sw_t, dx=dx, gran=B), f)
+    timed("block wgrad 8192x8192x16384",
+          lambda: m.fp8_linear_wgrad(qg_t, qx_t, sg_t, sx_t, dw=dw, gran=B), f)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mlp_8192x4096x14336.txt")
@@ -678,6 +740,9 @@ def main():
         return
     if args.data_sensitivity:
         data_sensitivity(shape=tuple(int(v) for v in args.shape.split(",")))
+        return
+    if args.profile_gemms:
+        profile_gemms()
         return
 
     import torch
