@@ -1236,6 +1236,308 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Block-recipe kernel for one weight scale per 128 x 128 block (forward and input
+// gradient): 256x256 tiles, 8 waves (two per SIMD) of 128x64, each an 8x4 grid of 16x16
+// tiles. gemm_fp8_mx16b_kernel's 256x128 tile is bound by its operand loads; this tile
+// loads a third fewer bytes per product. The folds are that kernel's (acc += P * sa * sb
+// after every 16x16x128 MFMA, the accumulators in VGPRs); what gives is the fragment
+// storage: a wave holds its stage's 4 B fragments and streams the 8 A rows through a ring
+// of 4 registers sets, two rows ahead, and replaces each B fragment by the next stage's
+// right after its last MFMA.
+// Two LDS slots. The barrier comes after 24 of a stage's 32 MFMAs, once every wave has
+// read all of the stage's A rows: it publishes stage s + 1 (whose first A rows and B
+// fragments are read during the last 8 MFMAs) and frees stage s's slot for the loads of
+// stage s + 2, issued during those same 8 MFMAs. The stage's scales sit behind its
+// operands in the slot, one 4-byte LDS load per wave: p = 64 w + l < 256 holds sa of tile
+// row 128 (p / 128) + 16 (p % 8) + (p % 128) / 8 (a lane's 8 row scales are contiguous),
+// p = 256 + c the weight scale of the tile's column block c (c = 0, 1).
+template <bool PAD>
+__global__ void __launch_bounds__(512, 1)
+gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                       const float* __restrict__ sa, const float* __restrict__ sb,
+                       uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
+                       int tiles_n, int split_m, int split_n) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4, kWaves = WM * WN, GROUP_M = 8;
+  constexpr int WTM = BM / WM, WTN = BN / WN;           // 128 x 64
+  constexpr int RT = WTM / 16, CT = WTN / 16;           // 8 x 4
+  constexpr int kRing = 4;                              // A row registers
+  constexpr int kTileBytes = (BM + BN) * kStageK;       // 64 KB
+  constexpr int kScaleOff = kTileBytes;
+  constexpr int SB = kTileBytes + 4 * 64 * kWaves;      // + one 4-byte lane per thread
+  constexpr int kRowsPerInst = 1024 / kStageK;          // 8 rows of 128 bytes
+  constexpr int kInstA = BM / (kRowsPerInst * kWaves);  // 4
+  constexpr int kInstB = BN / (kRowsPerInst * kWaves);  // 4
+  constexpr int kDma = kInstA + kInstB + 1;             // + one scale piece
+  constexpr int kStores = RT * CT / 2;
+  constexpr int kMf = RT * CT;                          // MFMAs per stage
+  constexpr int kBarrierAt = (RT - 2) * CT;             // MFMAs before the barrier
+  constexpr int kTail = kMf - kBarrierAt;
+  constexpr int L = 2;                                  // fold lag (MFMAs)
+  static_assert(kDma + kStores <= 63, "memory counts");
+  static_assert(2 * SB <= 160 * 1024, "LDS");
+  static_assert(WTN <= 128 && 128 % WTN == 0, "one weight scale per wave");
+  static_assert(kRing == 4 && RT % kRing == 0, "ring slots: row i in i % 4, and so the next "
+                "stage's rows 0 and 1 go where rows RT - 4 and RT - 3 were");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SB];
+  uint8_t* const slot0 = smem;
+  uint8_t* const slot1 = smem + SB;
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int kblocks = K / kStageK;
+  const v4i rsA = make_rsrc(A, (uint32_t)(M * K));
+  const v4i rsB = make_rsrc(B, (uint32_t)(N * K));
+  const v4i rsSa = make_rsrc(sa, (uint32_t)(M * kblocks * 4));
+  const v4i rsSb = make_rsrc(sb, (uint32_t)(((N + 127) / 128) * kblocks * 4));
+  const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc(D, 0, M * N * 2, kRsrcWord3);
+
+  // tile assignment: as in gemm_fp8_persist_kernel (one rectangle of tiles per XCD)
+  const int nwg = gridDim.x;
+  int bm0 = 0, bn0 = 0, bmc = tiles_m, bnc = tiles_n, slot = blockIdx.x, nslots = nwg;
+  if (split_m > 0) {
+    const int xcd = blockIdx.x & 7;
+    const int rm = (tiles_m + split_m - 1) / split_m, rn = (tiles_n + split_n - 1) / split_n;
+    const int bx = xcd / split_n, by = xcd % split_n;
+    bm0 = bx * rm;
+    bn0 = by * rn;
+    bmc = max(0, min(tiles_m, bm0 + rm) - bm0);
+    bnc = max(0, min(tiles_n, bn0 + rn) - bn0);
+    slot = blockIdx.x >> 3;
+    nslots = nwg >> 3;
+  }
+  const int block_tiles = bmc * bnc;
+  const int count = slot < block_tiles ? (block_tiles - slot + nslots - 1) / nslots : 0;
+  auto tile_mn = [&](int ti, int& m0, int& n0) {
+    const int lid = slot + ti * nslots;
+    const int per_group = GROUP_M * bnc;
+    const int group = lid / per_group;
+    const int first_m = group * GROUP_M;
+    const int gsize = min(bmc - first_m, GROUP_M);
+    const int in_group = lid - group * per_group;
+    m0 = (bm0 + first_m + in_group % gsize) * BM;
+    n0 = (bn0 + in_group / gsize) * BN;
+  };
+
+  // operand load plan: as gemm_fp8_mx16_kernel's
+  const int lrow = kRowsPerInst * wave + (lane >> 3);
+  const int lchunk = (lane & 7) ^ row_swizzle(lrow);
+  const uint32_t inst_rows = (uint32_t)(kRowsPerInst * kWaves) * (uint32_t)K;
+  const uint32_t lane_off = (uint32_t)lrow * (uint32_t)K + 16u * lchunk;
+  // scale load plan (see above): waves 0 .. 3 read sa, wave 4 the two weight scales
+  const int p = 64 * wave + lane;
+  const bool sc_from_a = wave < BM / 64;
+  uint32_t sc_lane = kOutOfRange;
+  if (p < BM) {
+    const int row = (p / WTM) * WTM + 16 * (p % RT) + (p % WTM) / RT;
+    sc_lane = (uint32_t)row * (uint32_t)kblocks * 4u;
+  } else if (p < BM + BN / 128) {
+    sc_lane = (uint32_t)(p - BM) * (uint32_t)kblocks * 4u;
+  }
+  struct Rows { uint32_t a, b, sc; };   // wave-uniform parts for the tile (K block 0)
+  auto rows_of = [&](int ti) -> Rows {
+    if (ti >= count) return {kOutOfRange, kOutOfRange, kOutOfRange};
+    int m0, n0;
+    tile_mn(ti, m0, n0);
+    const uint32_t sc = sc_from_a ? (uint32_t)m0 * (uint32_t)kblocks * 4u
+                                  : (uint32_t)(n0 / 128) * (uint32_t)kblocks * 4u;
+    return {(uint32_t)m0 * (uint32_t)K, (uint32_t)n0 * (uint32_t)K, sc};
+  };
+  // load d of stage kb (whole row offsets in the VGPR operand, which the buffer range check
+  // tests: rows past M or N read zeros; the K block's offset in the SGPR operand)
+  auto dma = [&](int d, uint8_t* slot_mem, Rows r, int kb) {
+    const uint32_t k0 = (uint32_t)kb * kStageK;
+    // PAD (an odd count of K blocks): the padding stage reads zeros, its scales too
+    const bool kin = !PAD || kb < kblocks;
+    const uint32_t lds = lds_addr(slot_mem);
+    if (d < kInstA)
+      dma16_so(rsA, kin ? lane_off + (r.a + d * inst_rows) : kOutOfRange, k0,
+               lds + 1024u * wave + 1024u * kWaves * d);
+    else if (d < kInstA + kInstB)
+      dma16_so(rsB, kin ? lane_off + (r.b + (d - kInstA) * inst_rows) : kOutOfRange, k0,
+               lds + BM * kStageK + 1024u * wave + 1024u * kWaves * (d - kInstA));
+    else
+      dma4(sc_from_a ? rsSa : rsSb,
+           (!kin || sc_lane == kOutOfRange || r.sc == kOutOfRange) ? kOutOfRange
+                                                                    : sc_lane + r.sc + 4u * kb,
+           lds + kScaleOff + 256u * wave);
+  };
+
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int sw = row_swizzle(r16);
+  // the lane's two 16-byte pieces of its fragment row, as offsets into a slot
+  const uint32_t fa0 = (uint32_t)(wm * WTM + r16) * kStageK + 16 * ((2 * g4) ^ sw);
+  const uint32_t fa1 = (uint32_t)(wm * WTM + r16) * kStageK + 16 * ((2 * g4 + 1) ^ sw);
+  const uint32_t fb0 = fa0 + (uint32_t)(BM + wn * WTN - wm * WTM) * kStageK;
+  const uint32_t fb1 = fa1 + (uint32_t)(BM + wn * WTN - wm * WTM) * kStageK;
+  static_assert((BM + BN) * kStageK <= 65536, "row offsets fit the LDS offset field");
+  auto rd = [&](uint32_t lo_at, uint32_t hi_at) {
+    const v4u lo = lds16(lo_at);
+    const v4u hi = lds16(hi_at);
+    v8i v;
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    return v;
+  };
+  struct Bases { uint32_t a0, a1, b0, b1; };
+  auto slot_addr = [&](const uint8_t* sm) {   // the slot's LDS address, one SGPR
+    uint32_t b = lds_addr(sm);
+    asm volatile("" : "+s"(b));
+    return b;
+  };
+  auto bases = [&](const uint8_t* sm) {
+    const uint32_t b = slot_addr(sm);
+    Bases q{b + fa0, b + fa1, b + fb0, b + fb1};
+    asm volatile("" : "+v"(q.a0), "+v"(q.a1), "+v"(q.b0), "+v"(q.b1));
+    return q;
+  };
+  auto rdA = [&](const Bases& q, int i) {
+    return rd(q.a0 + 16u * i * kStageK, q.a1 + 16u * i * kStageK);
+  };
+  auto rdB = [&](const Bases& q, int j) {
+    return rd(q.b0 + 16u * j * kStageK, q.b1 + 16u * j * kStageK);
+  };
+  // this stage's scales: fa[i] = sa of the lane's row in tile row i times the wave's
+  // weight scale
+  float fa[RT];
+  const uint32_t fsa = kScaleOff + 4u * (uint32_t)(wm * WTM + r16 * RT);
+  const uint32_t fsb = kScaleOff + 4u * (uint32_t)(BM + (wn * WTN) / 128);
+  auto rd_scales = [&](const uint8_t* sm) {
+    static_assert(RT % 4 == 0, "row scales by 16 bytes");
+    uint32_t ba = slot_addr(sm) + fsa;
+    asm volatile("" : "+v"(ba));
+#pragma unroll
+    for (int v = 0; v < RT / 4; ++v) {
+      const v4u a4 = lds16(ba + 16u * v);
+      fa[4 * v + 0] = __uint_as_float(a4.x); fa[4 * v + 1] = __uint_as_float(a4.y);
+      fa[4 * v + 2] = __uint_as_float(a4.z); fa[4 * v + 3] = __uint_as_float(a4.w);
+    }
+    const float fb = *reinterpret_cast<const float*>(sm + fsb);
+#pragma unroll
+    for (int i = 0; i < RT; ++i) fa[i] *= fb;
+  };
+
+  v4f acc[RT][CT];
+  v8i Bq[CT], Aq[kRing];
+  const int ns = max(4, (kblocks + 1) & ~1);   // stages per tile: even, at least 4
+  Rows cur = rows_of(0), nxt = rows_of(1);
+
+  auto fold = [&](auto FIRST_, int x, const v4f& P) {
+    constexpr bool FIRST = decltype(FIRST_)::value != 0;
+    const int i = x / CT, j = x % CT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      acc[i][j][r] = FIRST ? P[r] * fa[i] : fmaf(P[r], fa[i], acc[i][j][r]);
+  };
+
+  // stage s from slot `mine`; `other` receives stage s + 1 (published by this stage's
+  // barrier). On entry Bq holds the stage's B fragments and Aq[0], Aq[1] its A rows 0, 1.
+  // AFTER: the first stage after a tile's epilogue, whose stores were issued after the
+  // loads of stage s + 1 and may stay in flight at the barrier.
+  auto stage = [&](auto FIRST_, int s, uint8_t* mine, uint8_t* other, bool after) {
+    const v4f z = {};
+    v4f P[L + 1];
+    const Bases qm = bases(mine);
+    rd_scales(mine);
+    const int gs = s + 2;
+    const Rows r = gs < ns ? cur : nxt;
+    const int kb = gs < ns ? gs : gs - ns;
+    Bases qo{};
+#pragma unroll
+    for (int x = 0; x < kMf; ++x) {
+      const int i = x / CT, j = x % CT;
+      P[x % (L + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bq[j], Aq[i % kRing], z,
+                                                                        0, 0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (x >= L) fold(FIRST_, x - L, P[(x - L) % (L + 1)]);
+      // this stage's A rows, two ahead
+      if (j == 0 && i + 2 < RT) Aq[(i + 2) % kRing] = rdA(qm, i + 2);
+      if (x == kBarrierAt - 1) {
+        // every A row of this stage read; stage s + 1 landed (own loads); then for all
+        if (after) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kStores) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        qo = bases(other);
+      }
+      if (x >= kBarrierAt) {
+        const int y = x - kBarrierAt;
+        // the loads of stage s + 2 into this stage's slot
+#pragma unroll
+        for (int d = y * kDma / kTail; d < (y + 1) * kDma / kTail; ++d) dma(d, mine, r, kb);
+        // the next stage's A rows 0 and 1, into the ring slots of rows RT - 4, RT - 3
+        if (y == 0) Aq[0] = rdA(qo, 0);
+        if (y == CT) Aq[1] = rdA(qo, 1);
+        // B fragment j after its last MFMA
+        if (i == RT - 1) Bq[j] = rdB(qo, j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int x = kMf - L; x < kMf; ++x) fold(FIRST_, x, P[x % (L + 1)]);
+  };
+
+  auto epilogue = [&](int m0, int n0) {
+    const int mrow = m0 + wm * WTM + r16;
+    const int ncol = n0 + wn * WTN + 16 * (g4 & 1) + 8 * (g4 >> 1);
+    const uint32_t base = ((uint32_t)mrow * (uint32_t)N + (uint32_t)ncol) * 2u;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int m = mrow + 16 * i;
+      const bool live = m < M_valid;   // rows past it are written as zeros, whatever
+                                       // their sums hold (a select, not a product)
+#pragma unroll
+      for (int jp = 0; jp < CT / 2; ++jp) {
+        const int j = 2 * jp;
+        const uint32_t p0j = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        const uint32_t p1j = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        const uint32_t p0k = pack_bf16x2(acc[i][j + 1][0], acc[i][j + 1][1]);
+        const uint32_t p1k = pack_bf16x2(acc[i][j + 1][2], acc[i][j + 1][3]);
+        const auto w0 = __builtin_amdgcn_permlane16_swap(p0j, p0k, false, false);
+        const auto w1 = __builtin_amdgcn_permlane16_swap(p1j, p1k, false, false);
+        v4i o = {(int)w0[0], (int)w1[0], (int)w0[1], (int)w1[1]};
+        if (!live) o = v4i{0, 0, 0, 0};
+        const bool in = m < M && ncol + 32 * jp < N;
+        const uint32_t off =
+            in ? base + (uint32_t)(16 * i) * (uint32_t)N * 2u + 64u * jp : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(o, rsD, off, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) dma(d, slot0, cur, 0);
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) dma(d, slot1, cur, 1);
+  wait_vm<kDma>();                     // stage 0 landed
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  {
+    const Bases q = bases(slot0);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) Bq[j] = rdB(q, j);
+    Aq[0] = rdA(q, 0);
+    Aq[1] = rdA(q, 1);
+  }
+  for (int ti = 0; ti < count; ++ti) {
+    int cm0, cn0;
+    tile_mn(ti, cm0, cn0);
+    // stages 0, 1 | 2 .. ns - 1 in pairs (ns is even and at least 4)
+    stage(IC<1>{}, 0, slot0, slot1, ti > 0);
+    stage(IC<0>{}, 1, slot1, slot0, false);
+    for (int s = 2; s < ns; s += 2) {
+      stage(IC<0>{}, s, slot0, slot1, false);
+      stage(IC<0>{}, s + 1, slot1, slot0, false);
+    }
+    epilogue(cm0, cn0);
+    cur = nxt;
+    nxt = rows_of(ti + 2);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // no load may land after exit
+}
+
+// ---------------------------------------------------------------------------
 // One tile per workgroup; K steps past the end are zero loads, so the loop body
 // (unrolled by STAGES) needs no branches. Tensorwise scaling only.
 template <class C>
@@ -1424,12 +1726,36 @@ hipError_t run_mx16b(const uint8_t* A, const uint8_t* B, const float* sa, const 
 // block recipe on the 16x16x128 kernel: 256x128 tiles, 8 waves of 64x64
 template <int BROWS> using BlkMx16 = PCfg<256, 128, 4, 2, 2, 0, 8, BROWS>;
 
+hipError_t run_mx16bw(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
+                      uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  const int tiles = tiles_m * tiles_n;
+  const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
+  int split_m = 0, split_n = 0;
+  if (grid == kMaxWorkgroups) xcd_split(tiles_m, tiles_n, 256, 256, split_m, split_n);
+  // an odd count of K blocks ends each tile with a padding stage (stages come in pairs)
+  if ((K / kStageK) % 2 == 0)
+    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<false>), dim3((unsigned)grid), dim3(512), 0, s, A,
+                       B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  else
+    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<true>), dim3((unsigned)grid), dim3(512), 0, s, A,
+                       B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  return hipGetLastError();
+}
+
 template <int BROWS>
 hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
                      uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
   // K is a multiple of 128 (checked on the host), so the step count is even
   // (the per-row B scale variant keeps two stages: four run out of registers)
-  if (K >= 4 * kStageK) return run_mx16b<BlkMx16<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
+  if (K >= 4 * kStageK) {
+    // one weight scale per 128x128 block and enough 256x256 tiles to fill the chip: the
+    // wide-tile kernel
+    if constexpr (BROWS == 128)
+      if ((int64_t)((M + 255) / 256) * ((N + 255) / 256) >= kMaxWorkgroups)
+        return run_mx16bw(A, B, sa, sb, D, M, N, K, M_valid, s);
+    return run_mx16b<BlkMx16<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
+  }
   const int nk = K / kBKS;
   if constexpr (BROWS != 1)
     if (nk % 4 == 0)

@@ -97,6 +97,32 @@ def test_block_linear_step_wide_kernel(lib, M, K, N, rv):
     test_block_linear_step(lib, M, K, N, rv)
 
 
+@pytest.mark.parametrize("M,K,N,rv", [(4224, 640, 4096, 4200), (4224, 4096, 640, 4200)])
+def test_block_wide_tiles(lib, M, K, N, rv):
+    """Outputs of at least 256 tiles of 256x256 take the 256x256-tile kernel (one weight scale
+    per 128x128 block: forward, with y [M, N], and input gradient, with dx [M, K]): rows ragged
+    against the tiles, padded token rows, an odd count of 128-wide blocks (5) in the
+    contraction. Every output against both bounds (the tolerance and float32 accumulation)."""
+    test_block_linear_step(lib, M, K, N, rv)
+    d = workloads.linear_inputs(5, 0, M=M, K=K, N=N)
+    x, w, g = d["x"], d["w"], d["g"]
+    B = lib.FP8_BLOCK_1x128
+    qx, _, _, sx, _ = lib.fp8_quantize_amax(dev_bf16(x), rows_valid=rv, gran=B)
+    qw, qw_t, _, sw, sw_t = lib.fp8_quantize_amax(dev_bf16(w), gran=lib.FP8_BLOCK_128x128)
+    qg, _, _, sg, _ = lib.fp8_quantize_amax(dev_bf16(g), rows_valid=rv, gran=B)
+    wide = [("fwd", lib.fp8_linear_fwd(qx, qw, sx, sw, M_valid=rv, gran=B), qx, qw, sx, sw)] \
+        if N >= 4096 else \
+        [("dgrad", lib.fp8_linear_dgrad(qg, qw_t, sg, sw_t, M_valid=rv, gran=B), qg, qw_t, sg, sw_t)]
+    torch.cuda.synchronize()
+    for what, out, qa, qb, sa, sb in wide:
+        note(f"block wide tiles: {what} {M}x{K}x{N}, tight bound")
+        got = host_bf16_f64(out)
+        assert np.all(got[rv:] == 0), what
+        qah, sah = host_u8(qa)[:rv], sa.cpu().numpy().astype(np.float64)[:rv]
+        D, tight = block.block_fp32_bound(qah, host_u8(qb), sah, sb.cpu().numpy().astype(np.float64), 128)
+        assert_within(got[:rv], D, tight, f"block {what} (float32 accumulation)")
+
+
 def test_block_full_size_sampled(lib):
     """The block recipe at its benchmark size (M=16384, K=N=8192, outliers x100 at 1%):
     tile grids bit-exact on sampled tiles, GEMM outputs on sampled elements."""
