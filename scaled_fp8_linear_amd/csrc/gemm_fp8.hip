@@ -1247,40 +1247,49 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
 // Two LDS slots. The barrier comes after 24 of a stage's 32 MFMAs, once every wave has
 // read all of the stage's A rows: it publishes stage s + 1 (whose first A rows and B
 // fragments are read during the last 8 MFMAs) and frees stage s's slot for the loads of
-// stage s + 2, issued during those same 8 MFMAs. The stage's scales sit behind its
-// operands in the slot, one 4-byte LDS load per wave: p = 64 w + l < 256 holds sa of tile
-// row 128 (p / 128) + 16 (p % 8) + (p % 128) / 8 (a lane's 8 row scales are contiguous),
-// p = 256 + c the weight scale of the tile's column block c (c = 0, 1).
-template <bool PAD>
+// stage s + 2, issued during those same 8 MFMAs.
+// Scales: lane p = 64 w + l of the workgroup loads the scales of one tile row for p < 256
+// and, for p = 256 + c, the weight scale of the tile's column block c.
+// SG (a count of K blocks divisible by 4): lane p < 256 loads row p's scales of 4
+// consecutive K blocks (16 bytes) once per 4 stages into one of two LDS regions (a quarter
+// of the requests of one 4-byte load per stage: the scale loads are scattered, one row
+// apart). Else the stage's scales are 4-byte loads behind its operands in the slot, lane p
+// holding row 128 (p / 128) + 16 (p % 8) + (p % 128) / 8, so that a lane's 8 row scales
+// are neighbours.
+template <bool PAD, bool SG>
 __global__ void __launch_bounds__(512, 1)
 gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                        const float* __restrict__ sa, const float* __restrict__ sb,
                        uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
                        int tiles_n, int split_m, int split_n) {
+  static_assert(!(PAD && SG), "grouped scales need a K block count divisible by 4");
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4, kWaves = WM * WN, GROUP_M = 8;
   constexpr int WTM = BM / WM, WTN = BN / WN;           // 128 x 64
   constexpr int RT = WTM / 16, CT = WTN / 16;           // 8 x 4
   constexpr int kRing = 4;                              // A row registers
   constexpr int kTileBytes = (BM + BN) * kStageK;       // 64 KB
-  constexpr int kScaleOff = kTileBytes;
-  constexpr int SB = kTileBytes + 4 * 64 * kWaves;      // + one 4-byte lane per thread
+  constexpr int kScaleOff = kTileBytes;                 // !SG: 4 bytes per lane
+  constexpr int SB = kTileBytes + (SG ? 0 : 4 * 64 * kWaves);
+  constexpr int kRegion = 16 * 64 * kWaves;             // SG: 16 bytes per lane
   constexpr int kRowsPerInst = 1024 / kStageK;          // 8 rows of 128 bytes
   constexpr int kInstA = BM / (kRowsPerInst * kWaves);  // 4
   constexpr int kInstB = BN / (kRowsPerInst * kWaves);  // 4
-  constexpr int kDma = kInstA + kInstB + 1;             // + one scale piece
+  constexpr int kDma = kInstA + kInstB + (SG ? 0 : 1);  // + the stage's scale piece
   constexpr int kStores = RT * CT / 2;
   constexpr int kMf = RT * CT;                          // MFMAs per stage
   constexpr int kBarrierAt = (RT - 2) * CT;             // MFMAs before the barrier
   constexpr int kTail = kMf - kBarrierAt;
   constexpr int L = 2;                                  // fold lag (MFMAs)
-  static_assert(kDma + kStores <= 63, "memory counts");
-  static_assert(2 * SB <= 160 * 1024, "LDS");
+  constexpr int kGroup = 4;                             // SG: stages per scale load
+  static_assert(kDma + 1 + kStores <= 63, "memory counts");
+  static_assert(2 * SB + (SG ? 2 * kRegion : 0) <= 160 * 1024, "LDS");
   static_assert(WTN <= 128 && 128 % WTN == 0, "one weight scale per wave");
   static_assert(kRing == 4 && RT % kRing == 0, "ring slots: row i in i % 4, and so the next "
                 "stage's rows 0 and 1 go where rows RT - 4 and RT - 3 were");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SB + (SG ? 2 * kRegion : 0)];
   uint8_t* const slot0 = smem;
   uint8_t* const slot1 = smem + SB;
+  uint8_t* const regions = smem + 2 * SB;               // SG
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -1329,7 +1338,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   const bool sc_from_a = wave < BM / 64;
   uint32_t sc_lane = kOutOfRange;
   if (p < BM) {
-    const int row = (p / WTM) * WTM + 16 * (p % RT) + (p % WTM) / RT;
+    const int row = SG ? p : (p / WTM) * WTM + 16 * (p % RT) + (p % WTM) / RT;
     sc_lane = (uint32_t)row * (uint32_t)kblocks * 4u;
   } else if (p < BM + BN / 128) {
     sc_lane = (uint32_t)(p - BM) * (uint32_t)kblocks * 4u;
@@ -1342,6 +1351,10 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     const uint32_t sc = sc_from_a ? (uint32_t)m0 * (uint32_t)kblocks * 4u
                                   : (uint32_t)(n0 / 128) * (uint32_t)kblocks * 4u;
     return {(uint32_t)m0 * (uint32_t)K, (uint32_t)n0 * (uint32_t)K, sc};
+  };
+  auto sc_off = [&](Rows r, int kb) {
+    return (sc_lane == kOutOfRange || r.sc == kOutOfRange) ? kOutOfRange
+                                                           : sc_lane + r.sc + 4u * kb;
   };
   // load d of stage kb (whole row offsets in the VGPR operand, which the buffer range check
   // tests: rows past M or N read zeros; the K block's offset in the SGPR operand)
@@ -1356,11 +1369,14 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     else if (d < kInstA + kInstB)
       dma16_so(rsB, kin ? lane_off + (r.b + (d - kInstA) * inst_rows) : kOutOfRange, k0,
                lds + BM * kStageK + 1024u * wave + 1024u * kWaves * (d - kInstA));
-    else
-      dma4(sc_from_a ? rsSa : rsSb,
-           (!kin || sc_lane == kOutOfRange || r.sc == kOutOfRange) ? kOutOfRange
-                                                                    : sc_lane + r.sc + 4u * kb,
+    else if constexpr (!SG)
+      dma4(sc_from_a ? rsSa : rsSb, kin ? sc_off(r, kb) : kOutOfRange,
            lds + kScaleOff + 256u * wave);
+  };
+  // SG: the scales of K blocks kb .. kb + 3 (kb % 4 == 0) into region `rg` (0 or 1)
+  auto dma_scales = [&](int rg, Rows r, int kb) {
+    dma16(sc_from_a ? rsSa : rsSb, sc_off(r, kb),
+          lds_addr(regions) + (uint32_t)(rg * kRegion) + 1024u * wave);
   };
 
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -1400,19 +1416,33 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   // this stage's scales: fa[i] = sa of the lane's row in tile row i times the wave's
   // weight scale
   float fa[RT];
-  const uint32_t fsa = kScaleOff + 4u * (uint32_t)(wm * WTM + r16 * RT);
-  const uint32_t fsb = kScaleOff + 4u * (uint32_t)(BM + (wn * WTN) / 128);
-  auto rd_scales = [&](const uint8_t* sm) {
+  const int pa = wm * WTM + r16 * (SG ? 1 : RT);   // the lane's first row-scale lane
+  const int pb = BM + (wn * WTN) / 128;
+  auto rd_scales = [&](const uint8_t* sm, int rg, int q) {
     static_assert(RT % 4 == 0, "row scales by 16 bytes");
-    uint32_t ba = slot_addr(sm) + fsa;
-    asm volatile("" : "+v"(ba));
+    float fb;
+    if constexpr (SG) {
+      // lane p's 4 K blocks at 16 p .. 16 p + 15 of the region; this stage's is the q-th.
+      // Tile row i of the lane is lane pa + 16 i, so the 16 rows a read serves lie 16
+      // bytes apart: 16 distinct banks.
+      typedef const __attribute__((address_space(3))) float lds_f32;
+      uint32_t ba = slot_addr(regions) + (uint32_t)(rg * kRegion) + 16u * pa + 4u * q;
+      asm volatile("" : "+v"(ba));
 #pragma unroll
-    for (int v = 0; v < RT / 4; ++v) {
-      const v4u a4 = lds16(ba + 16u * v);
-      fa[4 * v + 0] = __uint_as_float(a4.x); fa[4 * v + 1] = __uint_as_float(a4.y);
-      fa[4 * v + 2] = __uint_as_float(a4.z); fa[4 * v + 3] = __uint_as_float(a4.w);
+      for (int i = 0; i < RT; ++i) fa[i] = *(lds_f32*)(uintptr_t)(ba + 256u * i);
+      fb = *(lds_f32*)(uintptr_t)(slot_addr(regions) + (uint32_t)(rg * kRegion) + 16u * pb +
+                                  4u * q);
+    } else {
+      uint32_t ba = slot_addr(sm) + kScaleOff + 4u * pa;
+      asm volatile("" : "+v"(ba));
+#pragma unroll
+      for (int v = 0; v < RT / 4; ++v) {
+        const v4u a4 = lds16(ba + 16u * v);
+        fa[4 * v + 0] = __uint_as_float(a4.x); fa[4 * v + 1] = __uint_as_float(a4.y);
+        fa[4 * v + 2] = __uint_as_float(a4.z); fa[4 * v + 3] = __uint_as_float(a4.w);
+      }
+      fb = *reinterpret_cast<const float*>(sm + kScaleOff + 4 * pb);
     }
-    const float fb = *reinterpret_cast<const float*>(sm + fsb);
 #pragma unroll
     for (int i = 0; i < RT; ++i) fa[i] *= fb;
   };
@@ -1421,6 +1451,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   v8i Bq[CT], Aq[kRing];
   const int ns = max(4, (kblocks + 1) & ~1);   // stages per tile: even, at least 4
   Rows cur = rows_of(0), nxt = rows_of(1);
+  int gq = 0;                                  // SG: scale groups begun before this tile
 
   auto fold = [&](auto FIRST_, int x, const v4f& P) {
     constexpr bool FIRST = decltype(FIRST_)::value != 0;
@@ -1433,15 +1464,22 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   // stage s from slot `mine`; `other` receives stage s + 1 (published by this stage's
   // barrier). On entry Bq holds the stage's B fragments and Aq[0], Aq[1] its A rows 0, 1.
   // AFTER: the first stage after a tile's epilogue, whose stores were issued after the
-  // loads of stage s + 1 and may stay in flight at the barrier.
-  auto stage = [&](auto FIRST_, int s, uint8_t* mine, uint8_t* other, bool after) {
+  // loads of stage s + 1 and may stay in flight at the barrier. SG: Q = s % 4; the tail of a
+  // stage with Q = 0 loads the scales of stages s + 4 .. s + 7 into the other region, the
+  // one that stages s - 4 .. s - 1 read (done by every wave at this stage's barrier).
+  auto stage = [&](auto FIRST_, auto Q_, int s, uint8_t* mine, uint8_t* other, bool after) {
+    constexpr int Q = decltype(Q_)::value;
     const v4f z = {};
     v4f P[L + 1];
     const Bases qm = bases(mine);
-    rd_scales(mine);
+    const int rg = (gq + s / kGroup) & 1;
+    rd_scales(mine, rg, Q);
     const int gs = s + 2;
     const Rows r = gs < ns ? cur : nxt;
     const int kb = gs < ns ? gs : gs - ns;
+    const int gs4 = s + kGroup;
+    const Rows r4 = gs4 < ns ? cur : nxt;
+    const int kb4 = gs4 < ns ? gs4 : gs4 - ns;
     Bases qo{};
 #pragma unroll
     for (int x = 0; x < kMf; ++x) {
@@ -1465,6 +1503,8 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
         // the loads of stage s + 2 into this stage's slot
 #pragma unroll
         for (int d = y * kDma / kTail; d < (y + 1) * kDma / kTail; ++d) dma(d, mine, r, kb);
+        if constexpr (SG && Q == 0)
+          if (y == kTail - 1) dma_scales(rg ^ 1, r4, kb4);
         // the next stage's A rows 0 and 1, into the ring slots of rows RT - 4, RT - 3
         if (y == 0) Aq[0] = rdA(qo, 0);
         if (y == CT) Aq[1] = rdA(qo, 1);
@@ -1506,11 +1546,12 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     }
   };
 
+  if constexpr (SG) dma_scales(0, cur, 0);
 #pragma unroll
   for (int d = 0; d < kDma; ++d) dma(d, slot0, cur, 0);
 #pragma unroll
   for (int d = 0; d < kDma; ++d) dma(d, slot1, cur, 1);
-  wait_vm<kDma>();                     // stage 0 landed
+  wait_vm<kDma>();                     // stage 0 landed (and SG: the first scale group)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   {
@@ -1523,12 +1564,27 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   for (int ti = 0; ti < count; ++ti) {
     int cm0, cn0;
     tile_mn(ti, cm0, cn0);
-    // stages 0, 1 | 2 .. ns - 1 in pairs (ns is even and at least 4)
-    stage(IC<1>{}, 0, slot0, slot1, ti > 0);
-    stage(IC<0>{}, 1, slot1, slot0, false);
-    for (int s = 2; s < ns; s += 2) {
-      stage(IC<0>{}, s, slot0, slot1, false);
-      stage(IC<0>{}, s + 1, slot1, slot0, false);
+    if constexpr (SG) {
+      // stages in fours (ns is a multiple of 4)
+      stage(IC<1>{}, IC<0>{}, 0, slot0, slot1, ti > 0);
+      stage(IC<0>{}, IC<1>{}, 1, slot1, slot0, false);
+      stage(IC<0>{}, IC<2>{}, 2, slot0, slot1, false);
+      stage(IC<0>{}, IC<3>{}, 3, slot1, slot0, false);
+      for (int s = 4; s < ns; s += 4) {
+        stage(IC<0>{}, IC<0>{}, s, slot0, slot1, false);
+        stage(IC<0>{}, IC<1>{}, s + 1, slot1, slot0, false);
+        stage(IC<0>{}, IC<2>{}, s + 2, slot0, slot1, false);
+        stage(IC<0>{}, IC<3>{}, s + 3, slot1, slot0, false);
+      }
+      gq += ns / kGroup;
+    } else {
+      // stages 0, 1 | 2 .. ns - 1 in pairs (ns is even and at least 4)
+      stage(IC<1>{}, IC<0>{}, 0, slot0, slot1, ti > 0);
+      stage(IC<0>{}, IC<0>{}, 1, slot1, slot0, false);
+      for (int s = 2; s < ns; s += 2) {
+        stage(IC<0>{}, IC<0>{}, s, slot0, slot1, false);
+        stage(IC<0>{}, IC<0>{}, s + 1, slot1, slot0, false);
+      }
     }
     epilogue(cm0, cn0);
     cur = nxt;
@@ -1733,13 +1789,19 @@ hipError_t run_mx16bw(const uint8_t* A, const uint8_t* B, const float* sa, const
   const int grid = tiles < kMaxWorkgroups ? tiles : kMaxWorkgroups;
   int split_m = 0, split_n = 0;
   if (grid == kMaxWorkgroups) xcd_split(tiles_m, tiles_n, 256, 256, split_m, split_n);
-  // an odd count of K blocks ends each tile with a padding stage (stages come in pairs)
-  if ((K / kStageK) % 2 == 0)
-    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<false>), dim3((unsigned)grid), dim3(512), 0, s, A,
-                       B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  // a count of K blocks divisible by 4 (and 16-byte aligned scale grids): scales in groups
+  // of 4 stages; an odd count ends each tile with a padding stage (stages come in pairs)
+  const int kblocks = K / kStageK;
+  if (kblocks % 4 == 0 && ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sb)) &
+                           15) == 0)
+    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<false, true>), dim3((unsigned)grid), dim3(512), 0,
+                       s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  else if (kblocks % 2 == 0)
+    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<false, false>), dim3((unsigned)grid), dim3(512),
+                       0, s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   else
-    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<true>), dim3((unsigned)grid), dim3(512), 0, s, A,
-                       B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<true, false>), dim3((unsigned)grid), dim3(512), 0,
+                       s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   return hipGetLastError();
 }
 
