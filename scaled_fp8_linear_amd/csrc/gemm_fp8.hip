@@ -788,7 +788,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     const Rows r = gs < ns ? cur : nxt;
     const int kb = gs < ns ? gs : gs - ns;
     constexpr int kSecond = RS * CT;                 // MFMAs in the second half
-    constexpr int kReads = CT + 1;                   // fragments to read
+    constexpr int kLeadA = CT - 1;                   // see the reads below
     constexpr int kEpLo = RH * kOps;                 // EPI = 1: store ops of rows 0 .. RH-1
     static_assert(EPI != 1 || kDma < kSecond, "the loads go out before the stores");
 #pragma unroll
@@ -807,10 +807,15 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
             op_store(k / kOps, k % kOps, op_value(k / kOps, k % kOps), em0, en0);
       } else {
         if (x * kDma / kSecond != (x + 1) * kDma / kSecond) dma(x * kDma / kSecond, mine, r, kb);
-        if (!LAST && x * kReads / kSecond != (x + 1) * kReads / kSecond) {
-          const int f = x * kReads / kSecond;
-          if (f < CT) Bn[f] = rdB(other, f);
-          else Alo[f - CT] = rdA(other, f - CT);
+        // the next stage's B fragments over the first kSecond - kLeadA MFMAs, then its A
+        // row 0, kLeadA MFMAs before the stage ends (late enough to take the registers of
+        // B fragments this half is done with, early enough that the next stage's first MFMA
+        // does not wait for it)
+        if constexpr (!LAST) {
+#pragma unroll
+          for (int f = 0; f < CT; ++f)
+            if (f * (kSecond - kLeadA) / CT == x) Bn[f] = rdB(other, f);
+          if (x == kSecond - kLeadA) Alo[0] = rdA(other, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
