@@ -1261,13 +1261,14 @@ gemm_fp8_mx16b_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
 // apart). Else the stage's scales are 4-byte loads behind its operands in the slot, lane p
 // holding row 128 (p / 128) + 16 (p % 8) + (p % 128) / 8, so that a lane's 8 row scales
 // are neighbours.
-template <bool PAD, bool SG>
+template <int BROWS, bool PAD, bool SG>
 __global__ void __launch_bounds__(512, 1)
 gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                        const float* __restrict__ sa, const float* __restrict__ sb,
                        uint16_t* __restrict__ D, int M, int N, int K, int M_valid, int tiles_m,
                        int tiles_n, int split_m, int split_n) {
   static_assert(!(PAD && SG), "grouped scales need a K block count divisible by 4");
+  static_assert(BROWS == 128 || (BROWS == 1 && SG), "per-row weight scales: grouped loads only");
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4, kWaves = WM * WN, GROUP_M = 8;
   constexpr int WTM = BM / WM, WTN = BN / WN;           // 128 x 64
   constexpr int RT = WTM / 16, CT = WTN / 16;           // 8 x 4
@@ -1303,7 +1304,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   const v4i rsA = make_rsrc(A, (uint32_t)(M * K));
   const v4i rsB = make_rsrc(B, (uint32_t)(N * K));
   const v4i rsSa = make_rsrc(sa, (uint32_t)(M * kblocks * 4));
-  const v4i rsSb = make_rsrc(sb, (uint32_t)(((N + 127) / 128) * kblocks * 4));
+  const v4i rsSb = make_rsrc(sb, (uint32_t)(((N + BROWS - 1) / BROWS) * kblocks * 4));
   const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc(D, 0, M * N * 2, kRsrcWord3);
 
   // tile assignment: as in gemm_fp8_persist_kernel (one rectangle of tiles per XCD)
@@ -1345,7 +1346,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   if (p < BM) {
     const int row = SG ? p : (p / WTM) * WTM + 16 * (p % RT) + (p % WTM) / RT;
     sc_lane = (uint32_t)row * (uint32_t)kblocks * 4u;
-  } else if (p < BM + BN / 128) {
+  } else if (p < BM + (BN + BROWS - 1) / BROWS) {
     sc_lane = (uint32_t)(p - BM) * (uint32_t)kblocks * 4u;
   }
   struct Rows { uint32_t a, b, sc; };   // wave-uniform parts for the tile (K block 0)
@@ -1354,7 +1355,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     int m0, n0;
     tile_mn(ti, m0, n0);
     const uint32_t sc = sc_from_a ? (uint32_t)m0 * (uint32_t)kblocks * 4u
-                                  : (uint32_t)(n0 / 128) * (uint32_t)kblocks * 4u;
+                                  : (uint32_t)(n0 / BROWS) * (uint32_t)kblocks * 4u;
     return {(uint32_t)m0 * (uint32_t)K, (uint32_t)n0 * (uint32_t)K, sc};
   };
   auto sc_off = [&](Rows r, int kb) {
@@ -1418,14 +1419,16 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   auto rdB = [&](const Bases& q, int j) {
     return rd(q.b0 + 16u * j * kStageK, q.b1 + 16u * j * kStageK);
   };
-  // this stage's scales: fa[i] = sa of the lane's row in tile row i times the wave's
-  // weight scale
+  // this stage's scales: fa[i] = sa of the lane's row in tile row i, times the wave's
+  // weight scale when B has one per 128x128 block; with one per B row (BROWS = 1),
+  // fb[4 j + r] = sb of the lane's column 4 g + r of tile column j
   float fa[RT];
+  float fb[BROWS == 1 ? 4 * CT : 1];
   const int pa = wm * WTM + r16 * (SG ? 1 : RT);   // the lane's first row-scale lane
-  const int pb = BM + (wn * WTN) / 128;
+  const int pb = BROWS == 1 ? BM + wn * WTN + 4 * g4 : BM + (wn * WTN) / 128;
   auto rd_scales = [&](const uint8_t* sm, int rg, int q) {
     static_assert(RT % 4 == 0, "row scales by 16 bytes");
-    float fb;
+    float fbw;
     if constexpr (SG) {
       // lane p's 4 K blocks at 16 p .. 16 p + 15 of the region; this stage's is the q-th.
       // Tile row i of the lane is lane pa + 16 i, so the 16 rows a read serves lie 16
@@ -1435,8 +1438,19 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
       asm volatile("" : "+v"(ba));
 #pragma unroll
       for (int i = 0; i < RT; ++i) fa[i] = *(lds_f32*)(uintptr_t)(ba + 256u * i);
-      fb = *(lds_f32*)(uintptr_t)(slot_addr(regions) + (uint32_t)(rg * kRegion) + 16u * pb +
-                                  4u * q);
+      uint32_t bb = slot_addr(regions) + (uint32_t)(rg * kRegion) + 16u * pb + 4u * q;
+      asm volatile("" : "+v"(bb));
+      if constexpr (BROWS == 1) {
+        // column 16 j + 4 g + r of the wave at 16 (BM + wn WTN + 16 j + 4 g + r) + 4 q: the 4
+        // lane groups read 4 addresses 64 bytes apart, the 16 lanes of a group one address
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) fb[4 * j + r] = *(lds_f32*)(uintptr_t)(bb + 256u * j + 16u * r);
+        return;
+      } else {
+        fbw = *(lds_f32*)(uintptr_t)bb;
+      }
     } else {
       uint32_t ba = slot_addr(sm) + kScaleOff + 4u * pa;
       asm volatile("" : "+v"(ba));
@@ -1446,10 +1460,10 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
         fa[4 * v + 0] = __uint_as_float(a4.x); fa[4 * v + 1] = __uint_as_float(a4.y);
         fa[4 * v + 2] = __uint_as_float(a4.z); fa[4 * v + 3] = __uint_as_float(a4.w);
       }
-      fb = *reinterpret_cast<const float*>(sm + kScaleOff + 4 * pb);
+      fbw = *reinterpret_cast<const float*>(sm + kScaleOff + 4 * pb);
     }
 #pragma unroll
-    for (int i = 0; i < RT; ++i) fa[i] *= fb;
+    for (int i = 0; i < RT; ++i) fa[i] *= fbw;
   };
 
   v4f acc[RT][CT];
@@ -1462,8 +1476,10 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     constexpr bool FIRST = decltype(FIRST_)::value != 0;
     const int i = x / CT, j = x % CT;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      acc[i][j][r] = FIRST ? P[r] * fa[i] : fmaf(P[r], fa[i], acc[i][j][r]);
+    for (int r = 0; r < 4; ++r) {
+      const float f = BROWS == 1 ? fa[i] * fb[4 * j + r] : fa[i];
+      acc[i][j][r] = FIRST ? P[r] * f : fmaf(P[r], f, acc[i][j][r]);
+    }
   };
 
   // stage s from slot `mine`; `other` receives stage s + 1 (published by this stage's
@@ -1787,6 +1803,13 @@ hipError_t run_mx16b(const uint8_t* A, const uint8_t* B, const float* sa, const 
 // block recipe on the 16x16x128 kernel: 256x128 tiles, 8 waves of 64x64
 template <int BROWS> using BlkMx16 = PCfg<256, 128, 4, 2, 2, 0, 8, BROWS>;
 
+// the 256x256 block-recipe kernel loads scales 4 K blocks (16 bytes) at a time
+bool bw_grouped(const float* sa, const float* sb, int K) {
+  return (K / kStageK) % 4 == 0 &&
+         ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sb)) & 15) == 0;
+}
+
+template <int BROWS>
 hipError_t run_mx16bw(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb,
                       uint16_t* D, int M, int N, int K, int M_valid, hipStream_t s) {
   const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
@@ -1796,17 +1819,18 @@ hipError_t run_mx16bw(const uint8_t* A, const uint8_t* B, const float* sa, const
   if (grid == kMaxWorkgroups) xcd_split(tiles_m, tiles_n, 256, 256, split_m, split_n);
   // a count of K blocks divisible by 4 (and 16-byte aligned scale grids): scales in groups
   // of 4 stages; an odd count ends each tile with a padding stage (stages come in pairs)
-  const int kblocks = K / kStageK;
-  if (kblocks % 4 == 0 && ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sb)) &
-                           15) == 0)
-    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<false, true>), dim3((unsigned)grid), dim3(512), 0,
-                       s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
-  else if (kblocks % 2 == 0)
-    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<false, false>), dim3((unsigned)grid), dim3(512),
-                       0, s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  const dim3 g((unsigned)grid), b(512);
+  if (bw_grouped(sa, sb, K))
+    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<BROWS, false, true>), g, b, 0, s, A, B, sa, sb, D, M,
+                       N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+  else if constexpr (BROWS == 1)
+    return hipErrorInvalidValue;   // the host takes this kernel only with grouped scales
+  else if ((K / kStageK) % 2 == 0)
+    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<BROWS, false, false>), g, b, 0, s, A, B, sa, sb, D,
+                       M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   else
-    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<true, false>), dim3((unsigned)grid), dim3(512), 0,
-                       s, A, B, sa, sb, D, M, N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
+    hipLaunchKernelGGL((gemm_fp8_mx16bw_kernel<BROWS, true, false>), g, b, 0, s, A, B, sa, sb, D, M,
+                       N, K, M_valid, tiles_m, tiles_n, split_m, split_n);
   return hipGetLastError();
 }
 
@@ -1816,11 +1840,11 @@ hipError_t run_block(const uint8_t* A, const uint8_t* B, const float* sa, const 
   // K is a multiple of 128 (checked on the host), so the step count is even
   // (the per-row B scale variant keeps two stages: four run out of registers)
   if (K >= 4 * kStageK) {
-    // one weight scale per 128x128 block and enough 256x256 tiles to fill the chip: the
-    // wide-tile kernel
-    if constexpr (BROWS == 128)
-      if ((int64_t)((M + 255) / 256) * ((N + 255) / 256) >= kMaxWorkgroups)
-        return run_mx16bw(A, B, sa, sb, D, M, N, K, M_valid, s);
+    // enough 256x256 tiles to fill the chip: the wide-tile kernel (with one scale per B row
+    // only when the scales load in groups of 4 K blocks)
+    if ((int64_t)((M + 255) / 256) * ((N + 255) / 256) >= kMaxWorkgroups &&
+        (BROWS == 128 || bw_grouped(sa, sb, K)))
+      return run_mx16bw<BROWS>(A, B, sa, sb, D, M, N, K, M_valid, s);
     return run_mx16b<BlkMx16<BROWS>>(A, B, sa, sb, D, M, N, K, M_valid, s);
   }
   const int nk = K / kBKS;

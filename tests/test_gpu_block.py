@@ -127,6 +127,26 @@ def test_block_wide_tiles(lib, M, K, N, rv):
         assert_within(got[:rv], D, tight, f"block {what} (float32 accumulation)")
 
 
+@pytest.mark.parametrize("M,K,N,rv", [(512, 4096, 4096, 500), (1536, 4096, 4352, 1536)])
+def test_block_wide_tiles_wgrad(lib, M, K, N, rv):
+    """Weight gradients dW [N, K] of at least 256 tiles of 256x256 take the 256x256-tile
+    kernel with one scale per B row (both operands carry per-row scales over 128-token
+    blocks), when the token count is a multiple of 512: 4 and 12 token blocks (one and three
+    scale groups per tile), padded tokens, ragged tiles. dW against both bounds."""
+    test_block_linear_step(lib, M, K, N, rv)
+    d = workloads.linear_inputs(5, 0, M=M, K=K, N=N)
+    B = lib.FP8_BLOCK_1x128
+    _, qx_t, _, _, sx_t = lib.fp8_quantize_amax(dev_bf16(d["x"]), rows_valid=rv, gran=B)
+    _, qg_t, _, _, sg_t = lib.fp8_quantize_amax(dev_bf16(d["g"]), rows_valid=rv, gran=B)
+    dw = lib.fp8_linear_wgrad(qg_t, qx_t, sg_t, sx_t, gran=B)
+    torch.cuda.synchronize()
+    note(f"block wide tiles: wgrad {N}x{K} over {M} tokens, tight bound")
+    D, tight = block.block_fp32_bound(host_u8(qg_t), host_u8(qx_t),
+                                      sg_t.cpu().numpy().astype(np.float64),
+                                      sx_t.cpu().numpy().astype(np.float64), 1)
+    assert_within(host_bf16_f64(dw), D, tight, "block wgrad (float32 accumulation)")
+
+
 def test_block_full_size_sampled(lib):
     """The block recipe at its benchmark size (M=16384, K=N=8192, outliers x100 at 1%):
     tile grids bit-exact on sampled tiles, GEMM outputs on sampled elements."""
