@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kBT = 128;                 // tile edge
 constexpr int kBThreads = 256;
+static_assert(kBThreads == 2 * kBT, "one lane per tile row and one per tile column");
 constexpr int kBColDwords = kBT / 4;     // 32 dwords per transposed column
 
 __device__ __forceinline__ int bslot(int c, int i) {
@@ -70,6 +71,8 @@ quantize_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
                       float* __restrict__ scale_t, int64_t tiles_c) {
   __shared__ uint32_t tile_t[kBT * kBColDwords];      // 16 KiB
   __shared__ uint32_t col_red[4][kBT];                 // per-wave column maxima
+  __shared__ uint32_t row_red[kBT];                    // row maxima
+  __shared__ float sinv_r[kBT], sinv_c[kBT];           // row and column multipliers
   __shared__ uint32_t tile_red[4];
 
   const int t = threadIdx.x;
@@ -130,31 +133,34 @@ quantize_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
 #pragma unroll
       for (int j = 0; j < 8; ++j) col_red[wave][8 * cc + j] = cmax[j];
     }
+    if (cc == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) row_red[8 * rg + i] = rmax[i];
+    }
+    __syncthreads();
+    // each scale once: lane t < 128 takes tile row t, lane 128 + c tile column c (rows and
+    // columns of a block tile are whole: both are multiples of 128)
+    if (t < kBT) {
+      const uint32_t m = row_red[t];
+      float s, si;
+      scale_pair(__uint_as_float(m << 16), &s, &si);
+      sinv_r[t] = si;
+      const int64_t r = row0 + t;
+      if (scale) scale[r * kblocks + tc] = s;
+      if (amax_out) amax_out[r * kblocks + tc] = __uint_as_float(m << 16);
+    } else {
+      const int c = t - kBT;
+      const uint32_t m = max(max(col_red[0][c], col_red[1][c]), max(col_red[2][c], col_red[3][c]));
+      float s, si;
+      scale_pair(__uint_as_float(m << 16), &s, &si);
+      sinv_c[c] = si;
+      if (scale_t) scale_t[(col0 + c) * rblocks + tr] = s;
+    }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = 8 * cc + j;
-      cmax[j] = max(max(col_red[0][c], col_red[1][c]), max(col_red[2][c], col_red[3][c]));
-    }
+    for (int i = 0; i < 8; ++i) rs_inv[i] = sinv_r[8 * rg + i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float s, si;
-      scale_pair(__uint_as_float(rmax[i] << 16), &s, &si);
-      rs_inv[i] = si;
-      const int64_t r = row0 + 8 * rg + i;
-      if (cc == 0 && r < rows) {
-        if (scale) scale[r * kblocks + tc] = s;
-        if (amax_out) amax_out[r * kblocks + tc] = __uint_as_float(rmax[i] << 16);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float s, si;
-      scale_pair(__uint_as_float(cmax[j] << 16), &s, &si);
-      cs_inv[j] = si;
-      const int64_t c = col + j;
-      if (rg == 0 && scale_t) scale_t[c * rblocks + tr] = s;
-    }
+    for (int j = 0; j < 8; ++j) cs_inv[j] = sinv_c[8 * cc + j];
   } else {
     uint32_t m = 0;
 #pragma unroll
