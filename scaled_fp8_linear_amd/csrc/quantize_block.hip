@@ -32,18 +32,7 @@ __device__ __forceinline__ int bslot(int c, int i) {
   return c * kBColDwords + (i ^ ((c >> 3) & (kBColDwords - 1)));
 }
 
-__device__ __forceinline__ uint32_t max8_bf16(uint4 v) {
-  uint32_t m0 = v.x & 0x7FFF7FFFu, m1 = v.y & 0x7FFF7FFFu;
-  uint32_t m2 = v.z & 0x7FFF7FFFu, m3 = v.w & 0x7FFF7FFFu;
-  uint32_t a = max(max(m0 & 0xFFFFu, m0 >> 16), max(m1 & 0xFFFFu, m1 >> 16));
-  uint32_t b = max(max(m2 & 0xFFFFu, m2 >> 16), max(m3 & 0xFFFFu, m3 >> 16));
-  return max(a, b);
-}
-
-__device__ __forceinline__ uint32_t col_abs(const uint4& v, int j) {
-  const uint32_t d = j < 2 ? (j == 0 ? v.x : v.y) : (j == 2 ? v.z : v.w);
-  return d;
-}
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 // 4 rows x 4 codes (one dword per row) -> 4 column dwords (rows 0..3 in bytes 0..3).
 __device__ __forceinline__ void transpose4x4(const uint32_t w0, const uint32_t w1,
@@ -93,21 +82,29 @@ quantize_block_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols
     v[i] = ok[i] ? ld_stream16(x + r * cols + col) : make_uint4(0, 0, 0, 0);
   }
 
-  // ---- per-row maxima (row tiles), per-column maxima (column tiles)
+  // ---- per-row maxima (row tiles), per-column maxima (column tiles): maxima of the 15-bit
+  // magnitudes, two columns at a time (packed 16-bit max over the 4 dwords of a row)
   uint32_t rmax[8];
+  us2 cm[4] = {us2{0, 0}, us2{0, 0}, us2{0, 0}, us2{0, 0}};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) rmax[i] = max8_bf16(v[i]);
+  for (int i = 0; i < 8; ++i) {
+    const us2 a = __builtin_bit_cast(us2, v[i].x & 0x7FFF7FFFu);
+    const us2 b = __builtin_bit_cast(us2, v[i].y & 0x7FFF7FFFu);
+    const us2 c = __builtin_bit_cast(us2, v[i].z & 0x7FFF7FFFu);
+    const us2 d = __builtin_bit_cast(us2, v[i].w & 0x7FFF7FFFu);
+    cm[0] = __builtin_elementwise_max(cm[0], a);
+    cm[1] = __builtin_elementwise_max(cm[1], b);
+    cm[2] = __builtin_elementwise_max(cm[2], c);
+    cm[3] = __builtin_elementwise_max(cm[3], d);
+    const us2 r = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                            __builtin_elementwise_max(c, d));
+    rmax[i] = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
   uint32_t cmax[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t d = col_abs(v[i], j >> 1);
-      const uint32_t h = (j & 1) ? (d >> 16) : (d & 0xFFFFu);
-      m = max(m, h & 0x7FFFu);
-    }
-    cmax[j] = m;
+  for (int j = 0; j < 4; ++j) {
+    cmax[2 * j] = cm[j][0];
+    cmax[2 * j + 1] = cm[j][1];
   }
 
   float rs_inv[8], cs_inv[8];
