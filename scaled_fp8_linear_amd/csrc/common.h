@@ -7,9 +7,7 @@
 namespace fp8lin {
 
 constexpr float kE4M3Max = 448.0f;     // largest finite OCP e4m3 value
-constexpr uint32_t kE4M3MaxBits = 0x43E00000u;   // 448.0f
 constexpr float kE5M2Max = 57344.0f;   // largest finite OCP e5m2 value (1.75 * 2^15)
-constexpr uint32_t kE5M2MaxBits = 0x47600000u;   // 57344.0f
 constexpr uint32_t kF32InfBits = 0x7F800000u;
 constexpr float kAmaxFloor = 1e-12f;   // lower clamp of amax before 448/amax
 
@@ -34,37 +32,26 @@ __device__ __forceinline__ void st_stream8(void* p, uint32_t a, uint32_t b) {
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
-// Saturate |v| > 448 (including +-inf) to +-448, keep NaN as it is. The
-// hardware converter is then only ever given values inside the e4m3 range or
-// NaN, so its own overflow behaviour never matters.
+// Clamp to +-448 (the e4m3 range; +-inf too) with one median-of-three, so the hardware
+// converter only ever sees values inside the range and its own overflow behaviour never
+// matters. A NaN comes out of the clamp as some finite value: quant4 marks NaN products
+// itself.
 __device__ __forceinline__ float sat_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t a = u & 0x7FFFFFFFu;
-  bool over = (a > kE4M3MaxBits) & (a <= kF32InfBits);
-  return over ? __uint_as_float((u & 0x80000000u) | kE4M3MaxBits) : v;
+  return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
 }
 
-// Two floats -> two OCP e4m3 codes (round to nearest even) in bits [15:0]
-// of the result (first argument in the low byte). gfx950's v_cvt_pk_fp8_f32
-// converts to the OCP E4M3 format.
-__device__ __forceinline__ uint32_t cvt2_e4m3(float a, float b) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false) & 0xFFFFu;
-}
-
-// Four floats -> four codes in one dword (a in the low byte).
+// Four floats -> four codes in one dword (a in the low byte). gfx950's
+// v_cvt_pk_fp8_f32 converts to the OCP E4M3 format, rounding to nearest even.
 __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), lo, true);
 }
 
 // OCP e5m2 (sign, 5 exponent bits with bias 15, 2 mantissa bits; 0x7C is infinity,
-// 0x7D..0x7F NaN), used for gradients in the hybrid format. Saturation at +-57344
-// as for e4m3, so the converter never sees an out-of-range value.
+// 0x7D..0x7F NaN), used for gradients in the hybrid format. Clamped to +-57344 as e4m3
+// is to +-448.
 __device__ __forceinline__ float sat_e5m2(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t a = u & 0x7FFFFFFFu;
-  bool over = (a > kE5M2MaxBits) & (a <= kF32InfBits);
-  return over ? __uint_as_float((u & 0x80000000u) | kE5M2MaxBits) : v;
+  return __builtin_amdgcn_fmed3f(v, -kE5M2Max, kE5M2Max);
 }
 
 // Four floats -> four OCP e5m2 codes in one dword (a in the low byte); gfx950's
@@ -81,46 +68,29 @@ __device__ __forceinline__ uint32_t sign_bytes(uint32_t d0, uint32_t d1) {
          (d1 & 0x80000000u);
 }
 
-// A NaN product is encoded as 0x7F with the sign of its input. The hardware
-// converter returns 0xFF for every NaN, and saturation keeps finite codes at
-// or below 0xFE, so a 0xFF byte marks exactly the NaN products.
-__device__ __forceinline__ uint32_t fix_nan_codes(uint32_t codes, uint32_t signs) {
-  const uint32_t ff = ((codes & 0x7F7F7F7Fu) + 0x01010101u) & codes & 0x80808080u;
-  if (__builtin_expect(ff != 0u, 0)) {
-    const uint32_t m = (ff >> 7) * 0xFFu;
-    codes = (codes & ~m) | (m & (0x7F7F7F7Fu | signs));
-  }
-  return codes;
-}
-
-// e5m2: after saturation every finite code is at most 0x7B in magnitude, so a
-// magnitude of 0x7D..0x7F marks a NaN product, whatever NaN code the converter
-// picked; it becomes 0x7F with the sign of its input, as for e4m3.
-__device__ __forceinline__ uint32_t fix_nan_codes_e5m2(uint32_t codes, uint32_t signs) {
-  const uint32_t ff = ((codes & 0x7F7F7F7Fu) + 0x03030303u) & 0x80808080u;
-  if (__builtin_expect(ff != 0u, 0)) {
-    const uint32_t m = (ff >> 7) * 0xFFu;
-    codes = (codes & ~m) | (m & (0x7F7F7F7Fu | signs));
-  }
-  return codes;
-}
-
-// Four bf16 inputs (packed in d0, d1) times their multipliers -> four codes.
-__device__ __forceinline__ uint32_t quant4(uint32_t d0, uint32_t d1, float s0, float s1, float s2,
-                                           float s3) {
-  const uint32_t c = cvt4_e4m3(bf16_lo(d0) * s0, bf16_hi(d0) * s1, bf16_lo(d1) * s2,
-                               bf16_hi(d1) * s3);
-  return fix_nan_codes(c, sign_bytes(d0, d1));
-}
-
-// The same in a chosen format: FMT 0 e4m3, 1 e5m2.
+// Four bf16 inputs (packed in d0, d1) times their multipliers -> four codes in the format
+// FMT (0 e4m3, 1 e5m2). A NaN product (a NaN input, or a multiplier that makes one) is
+// encoded as 0x7F with the sign of its input; the test is one compare per product, and
+// the fix-up runs only in lanes that have one.
 template <int FMT>
 __device__ __forceinline__ uint32_t quant4_fmt(uint32_t d0, uint32_t d1, float s0, float s1,
                                                float s2, float s3) {
-  if constexpr (FMT == 0) return quant4(d0, d1, s0, s1, s2, s3);
-  const uint32_t c = cvt4_e5m2(bf16_lo(d0) * s0, bf16_hi(d0) * s1, bf16_lo(d1) * s2,
-                               bf16_hi(d1) * s3);
-  return fix_nan_codes_e5m2(c, sign_bytes(d0, d1));
+  const float a = bf16_lo(d0) * s0, b = bf16_hi(d0) * s1;
+  const float c = bf16_lo(d1) * s2, d = bf16_hi(d1) * s3;
+  uint32_t codes = FMT == 0 ? cvt4_e4m3(a, b, c, d) : cvt4_e5m2(a, b, c, d);
+  const bool na = __builtin_isnan(a), nb = __builtin_isnan(b);
+  const bool nc = __builtin_isnan(c), nd = __builtin_isnan(d);
+  if (__builtin_expect(na | nb | nc | nd, 0)) {
+    const uint32_t m = (na ? 0xFFu : 0u) | (nb ? 0xFF00u : 0u) | (nc ? 0xFF0000u : 0u) |
+                       (nd ? 0xFF000000u : 0u);
+    codes = (codes & ~m) | (m & (0x7F7F7F7Fu | sign_bytes(d0, d1)));
+  }
+  return codes;
+}
+
+__device__ __forceinline__ uint32_t quant4(uint32_t d0, uint32_t d1, float s0, float s1, float s2,
+                                           float s3) {
+  return quant4_fmt<0>(d0, d1, s0, s1, s2, s3);
 }
 
 // Two floats -> two bf16 in one dword (a in the low half), round to nearest even
