@@ -404,13 +404,39 @@ def measure_config1(torch, m, workloads, iters=200, repeats=7):
     torch.cuda.synchronize()
     same = bool(torch.equal(y.view(torch.int16), ref.view(torch.int16)))
     graph_us = per_call_us(graph.replay)
+    # the same forward as one launch (amaxes, scales, casts and GEMM in one workgroup)
+    y1 = torch.empty((64, 128), dtype=torch.bfloat16, device=dev)
+    sc1 = torch.empty(4, **f32)
+    q1 = {"x": torch.empty((64, 128), dtype=torch.uint8, device=dev),
+          "w": torch.empty((128, 128), dtype=torch.uint8, device=dev)}
+
+    def fused():
+        m.fp8_linear_fwd_current(x, w, y=y1, scales=sc1, qx=q1["x"], qw=q1["w"])
+
+    fused_us = per_call_us(fused)
+    torch.cuda.synchronize()
+    fused_same = bool(torch.equal(q1["x"], q["x"]) and torch.equal(q1["w"], q["w"]) and
+                      torch.equal(sc1[:2], torch.cat([sc["x"], sc["w"]])) and
+                      torch.equal(sc1[2:], torch.cat([si["x"], si["w"]])))
+    gf = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        fused()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(gf):
+        fused()
+    fused_graph_us = per_call_us(gf.replay)
     flops = 2.0 * 64 * 128 * 128
     return {"workload": "one fp8 linear forward, current tensorwise scaling, x [64,128], "
                         "W [128,128] N(0,1): amax pass, scale, cast for x and W, then the GEMM",
             "launches": 7, "us_per_forward_eager": round(eager_us, 2),
             "us_per_forward_hip_graph": round(graph_us, 2),
             "graph_matches_eager": same,
-            "gflops_hip_graph": round(flops / (graph_us * 1e-6) / 1e9, 2)}
+            "gflops_hip_graph": round(flops / (graph_us * 1e-6) / 1e9, 2),
+            "one_launch": {"entry": "fp8_linear_fwd_current",
+                           "us_per_forward_eager": round(fused_us, 2),
+                           "us_per_forward_hip_graph": round(fused_graph_us, 2),
+                           "codes_and_scales_match_seven_launches": fused_same,
+                           "gflops_hip_graph": round(flops / (fused_graph_us * 1e-6) / 1e9, 2)}}
 
 
 def measure_config2(torch, m, repeats=5):
@@ -463,6 +489,61 @@ def measure_config2(torch, m, repeats=5):
             "steps": steps, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "ms_per_32_steps": round(ms, 4), "ms_per_step": round(ms / steps, 4),
             "repeats": repeats}
+
+
+def measure_bf16_step(torch, fp8_ms, steps=10, warmup=3):
+    """The same nine GEMMs of the MLP step in bf16 through torch (hipBLASLt), for context
+    beside the pages' expectation of about 2x from FP8 over bf16 when compute-bound: no
+    quantize, no scales, bf16 in and out, float32 accumulation. Right operands are
+    contiguous (the forward takes W^T stored as such); the wgrad's left operand is the
+    transposed view of g. Inputs are random bf16 of the step's shapes."""
+    M, K, N = 8192, 4096, 14336
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(9)
+
+    def r(*shape):
+        return torch.randn(*shape, device=dev, generator=gen).to(torch.bfloat16)
+
+    x, h = r(M, K), r(M, N)
+    wg, wu, wd = r(N, K), r(N, K), r(K, N)
+    wgt, wut, wdt = wg.t().contiguous(), wu.t().contiguous(), wd.t().contiguous()
+    gg, gu, gd = r(M, N), r(M, N), r(M, K)
+
+    def e(*shape):
+        return torch.empty(*shape, dtype=torch.bfloat16, device=dev)
+
+    yg, yu, yd = e(M, N), e(M, N), e(M, K)
+    dxg, dxu, dh = e(M, K), e(M, K), e(M, N)
+    dwg, dwu, dwd = e(N, K), e(N, K), e(K, N)
+
+    def step():
+        torch.mm(x, wgt, out=yg)
+        torch.mm(x, wut, out=yu)
+        torch.mm(h, wdt, out=yd)
+        torch.mm(gg, wg, out=dxg)
+        torch.mm(gu, wu, out=dxu)
+        torch.mm(gd, wd, out=dh)
+        torch.mm(gg.t(), x, out=dwg)
+        torch.mm(gu.t(), x, out=dwu)
+        torch.mm(gd.t(), h, out=dwd)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    flops = 18.0 * M * N * K
+    return {"workload": "the MLP step's nine GEMMs in bf16 (torch.mm, hipBLASLt), no quantize",
+            "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4),
+            "fp8_step_speedup": round(ms / fp8_ms, 3), "steps": steps}
 
 
 def measure_quantize_vs_copy(torch, m, reps=5):
@@ -910,6 +991,7 @@ def main():
             "block_recipe": measure_block_recipe(torch, m, workloads, max(3, args.steps // 3), 2),
             "packed_varlen_padding": measure_varlen(torch, m, workloads, max(3, args.steps // 3), 2),
             "autograd_bias_f1": measure_f1(torch, m, max(3, args.steps // 3), 2),
+            "bf16_gemm_step": measure_bf16_step(torch, line["ms_per_step"]),
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)

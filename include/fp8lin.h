@@ -244,6 +244,35 @@ int fp8_linear_wgrad(const void* qg_t, const void* qx_t, const float* sg, const 
                      int64_t M, int64_t N, int64_t K, int gran, void* stream);
 
 /*
+ * fp8_linear_fwd_current -- one current-scaling forward of a small linear in one
+ * launch: the amax of x and of W, their scales, the casts and the GEMM.
+ *
+ * Source: [SpecForge] Modifications (torchao Float8Linear with dynamic
+ * tensorwise scaling: amax first, then the scale, then the cast); [AstrAI]
+ * _update_delayed_scale (scale = amax/448, multiplier 448/amax, amax clamped
+ * at 1e-12) applied with no delay; [NeMo] reply on FP8 speedups (on very small
+ * matmuls the scaling overhead can exceed the gain, which is why this is one
+ * launch).
+ *
+ *   x       bf16 [M, K]; w bf16 [N, K]. M, N positive multiples of 16, K a
+ *           positive multiple of 128, and (M + N) * K <= 65536 (the operands'
+ *           codes fit one workgroup's LDS); larger linears use fp8_quantize_amax,
+ *           fp8_scale_update and fp8_linear_fwd (FP8_ERR_UNSUPPORTED says so).
+ *   y       bf16 [M, N] out: y[m,n] = bf16_rne(float32(sx * sw) *
+ *           sum_k qx[m,k] * qw[n,k]), float32 accumulation.
+ *   scales  float32 [4] out: {sx, sw, sx_inv, sw_inv}, each scale
+ *           max(amax, 1e-12)/448 and multiplier 448/max(amax, 1e-12), amax the
+ *           largest |value| of the whole tensor (NaN if any element is NaN).
+ *   qx, qw  e4m3 [M, K] and [N, K] out, or NULL: the codes (for a backward).
+ * All device pointers 16-byte aligned (scales: 4-byte). Same results, bit for
+ * bit in codes and scales, as fp8_quantize_amax (with a cleared amax),
+ * fp8_scale_update(FP8_SCALE_FROM_AMAX) and fp8_linear_fwd in sequence.
+ * Errors: FP8_ERR_SHAPE, FP8_ERR_UNSUPPORTED, FP8_ERR_NULL, FP8_ERR_ALIGN.
+ */
+int fp8_linear_fwd_current(const void* x, const void* w, int64_t M, int64_t N, int64_t K,
+                           void* y, float* scales, void* qx, void* qw, void* stream);
+
+/*
  * fp8_linear_fwd_bias -- fp8_linear_fwd with a bias added in the GEMM's epilogue.
  *
  * Source: [AstrAI] fp8_linear_forward(x, w, bias): the bias goes to the scaled

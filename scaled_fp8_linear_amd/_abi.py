@@ -27,7 +27,7 @@ FP8_A_E5M2 = 0x200              # flag for the GEMMs: the first operand holds E5
 EXPORTS = ("fp8_quantize_amax", "fp8_scale_update", "fp8_linear_fwd", "fp8_linear_dgrad",
            "fp8_linear_wgrad", "fp8_pad_tokens", "fp8_last_error", "fp8_version",
            "fp8_linear_fwd_bias", "fp8_bias_grad", "fp8_align_multiple", "fp8_pad_varlen",
-           "fp8_unpad_varlen")
+           "fp8_unpad_varlen", "fp8_linear_fwd_current")
 FP8_LAYOUT_THD, FP8_LAYOUT_BSHD = 0, 1
 
 
@@ -59,6 +59,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8_linear_fwd_bias.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                         _int, _vp]
     lib.fp8_bias_grad.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
+    lib.fp8_linear_fwd_current.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
     lib.fp8_linear_dgrad.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
     lib.fp8_linear_wgrad.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]
     lib.fp8_pad_tokens.argtypes = [_vp, _i64, _i64, _i32, _vp, ctypes.POINTER(_i64), _vp]
@@ -312,6 +313,37 @@ def fp8_linear_fwd(qx, qw, sx, sw, y=None, M_valid=None, gran=FP8_TENSORWISE, st
         _ptr(qx), _ptr(qw), _fptr(sx, "sx"), _fptr(sw, "sw"), _ptr(y), M, N, K, mv, gran,
         _stream(stream)))
     return y
+
+
+def fp8_linear_fwd_current(x, w, y=None, scales=None, qx=None, qw=None, want_codes=False,
+                           stream=None):
+    """One current-scaling forward of a small linear in one launch: amax of x [M, K] and of
+    w [N, K] (bf16), their scales, the casts, y [M, N] bf16. Returns (y, scales, qx, qw):
+    scales float32 [4] = {sx, sw, sx_inv, sw_inv}; qx, qw the e4m3 codes when passed or
+    ``want_codes``, else None."""
+    x, w = _bf16(x), _bf16(w)
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError(f"x {tuple(x.shape)} and w {tuple(w.shape)} must be [M, K] and [N, K]")
+    M, K = x.shape
+    N = w.shape[0]
+    dev = x.device
+    _need(x, "x", (M, K), _BF16_DTYPES, dev)
+    _need(w, "w", (N, K), _BF16_DTYPES, dev)
+    _need(y, "y", (M, N), _BF16_DTYPES, dev)
+    _need(scales, "scales", (4,), (torch.float32,), dev)
+    _need(qx, "qx", (M, K), (torch.uint8,), dev)
+    _need(qw, "qw", (N, K), (torch.uint8,), dev)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if scales is None:
+        scales = torch.empty(4, dtype=torch.float32, device=dev)
+    if want_codes and qx is None:
+        qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if want_codes and qw is None:
+        qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    _check("fp8_linear_fwd_current", load().fp8_linear_fwd_current(
+        _ptr(x), _ptr(w), M, N, K, _ptr(y), _ptr(scales), _ptr(qx), _ptr(qw), _stream(stream)))
+    return y, scales, qx, qw
 
 
 def fp8_bias_grad(g, rows_valid=None, db=None, stream=None):

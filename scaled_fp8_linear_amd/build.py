@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libfp8lin.so")
 ROOT = os.path.dirname(PKG)
 
 SOURCES = ["abi.cpp", "quantize_amax.hip", "quantize_block.hip", "scale_update.hip",
-           "pad_tokens.hip", "pad_varlen.hip", "gemm_fp8.hip", "bias.hip"]
+           "pad_tokens.hip", "pad_varlen.hip", "gemm_fp8.hip", "bias.hip", "linear_small.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

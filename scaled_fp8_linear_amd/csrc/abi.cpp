@@ -187,6 +187,29 @@ int fp8_linear_fwd(const void* qx, const void* qw, const float* sx, const float*
                     "fp8_linear_fwd");
 }
 
+int fp8_linear_fwd_current(const void* x, const void* w, int64_t M, int64_t N, int64_t K,
+                           void* y, float* scales, void* qx, void* qw, void* stream) {
+  const char* fn = "fp8_linear_fwd_current";
+  if (M < 16 || N < 16 || K < 128 || M % 16 || N % 16 || K % 128)
+    return fail(FP8_ERR_SHAPE,
+                "%s: M and N must be positive multiples of 16 and K a positive multiple of 128 "
+                "(got %lld x %lld x %lld)",
+                fn, (long long)M, (long long)N, (long long)K);
+  if ((M + N) * K > fp8lin::kSmallLinearCodes)
+    return fail(FP8_ERR_UNSUPPORTED,
+                "%s: (M + N) K = %lld bytes of codes exceed the one-workgroup limit of %d; use "
+                "fp8_quantize_amax, fp8_scale_update and fp8_linear_fwd",
+                fn, (long long)((M + N) * K), fp8lin::kSmallLinearCodes);
+  if (!x || !w || !y || !scales) return fail(FP8_ERR_NULL, "%s: NULL x, w, y or scales", fn);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(qx) || !aligned16(qw))
+    return fail(FP8_ERR_ALIGN, "%s: x, w, y, qx and qw must be 16-byte aligned", fn);
+  return hip_status(fp8lin::launch_linear_current_small(
+                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), (int)M,
+                        (int)N, (int)K, static_cast<uint16_t*>(y), scales,
+                        static_cast<uint8_t*>(qx), static_cast<uint8_t*>(qw), as_stream(stream)),
+                    fn);
+}
+
 int fp8_linear_fwd_bias(const void* qx, const void* qw, const float* sx, const float* sw,
                         const void* bias, void* y, int64_t M, int64_t N, int64_t K,
                         int64_t M_valid, int gran, void* stream) {

@@ -30,6 +30,13 @@ hipError_t launch_scale_update(int mode, float* amax, bool clear_amax, float* hi
                                int32_t pos, float* scale, float* scale_inv, bool e5m2,
                                hipStream_t s);
 
+// Current-scaling forward of a small linear in one workgroup: the operands' codes,
+// (M + N) K bytes, live in LDS between the cast and the GEMM.
+constexpr int kSmallLinearCodes = 64 * 1024;
+hipError_t launch_linear_current_small(const uint16_t* x, const uint16_t* w, int M, int N, int K,
+                                       uint16_t* y, float* scales, uint8_t* qx, uint8_t* qw,
+                                       hipStream_t s);
+
 hipError_t launch_pad_tokens(const uint16_t* x, int64_t T, int64_t cols, int64_t T_pad,
                              uint16_t* x_pad, hipStream_t s);
 

@@ -119,3 +119,13 @@ def test_padding_buffers():
             "length")
     # shapes right: stopped at the device check
     _raises(lambda: m.fp8_pad_varlen(x, cu, 4, 16), "device")
+
+
+def test_current_small_buffers():
+    x, w = torch.zeros((64, 128), dtype=bf), torch.zeros((128, 128), dtype=bf)
+    _raises(lambda: m.fp8_linear_fwd_current(x, torch.zeros((128, 64), dtype=bf)), "[M, K]")
+    _raises(lambda: m.fp8_linear_fwd_current(x, w, y=torch.empty((64, 64), dtype=bf)), "y ")
+    _raises(lambda: m.fp8_linear_fwd_current(x, w, scales=torch.empty(3, dtype=f32)), "scales")
+    _raises(lambda: m.fp8_linear_fwd_current(x, w, qx=torch.empty((64, 128), dtype=f32)), "qx")
+    _raises(lambda: m.fp8_linear_fwd_current(x, w, qw=torch.empty((128, 64), dtype=u8)), "qw")
+    _raises(lambda: m.fp8_linear_fwd_current(x, w), "device")

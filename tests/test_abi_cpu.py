@@ -81,6 +81,19 @@ def test_gemm_argument_checks(lib):
     assert lib.fp8_linear_wgrad(p, p, p, None, p, 16, 16, 16, 0, None) == 1          # NULL sx
 
 
+def test_current_small_argument_checks(lib):
+    p = ctypes.c_void_p(16)
+    f = lib.fp8_linear_fwd_current
+    assert f(p, p, 24, 128, 128, p, p, None, None, None) == 2           # M % 16
+    assert f(p, p, 64, 128, 64, p, p, None, None, None) == 2            # K % 128
+    assert f(p, p, 0, 128, 128, p, p, None, None, None) == 2            # empty
+    assert f(p, p, 256, 272, 128, p, p, None, None, None) == 4          # codes over 64 KiB
+    assert "65536" in _err(lib) and "fp8_linear_fwd" in _err(lib)
+    assert f(p, p, 64, 128, 128, None, p, None, None, None) == 1        # NULL y
+    assert f(p, p, 64, 128, 128, p, None, None, None, None) == 1        # NULL scales
+    assert f(p, p, 64, 128, 128, p, p, ctypes.c_void_p(8), None, None) == 3
+
+
 def test_quantize_argument_checks(lib):
     p = ctypes.c_void_p(16)
     assert lib.fp8_quantize_amax(None, 16, 16, 16, 0, p, p, p, p, None, None, None) == 1

@@ -1,0 +1,78 @@
+"""The one-launch current-scaling forward of a small linear (fp8_linear_fwd_current)
+against the oracle: amaxes, scales and multipliers bit for bit, the codes byte for byte,
+y within both GEMM bounds. Config 1 (x [64, 128], W [128, 128], N(0, 1)), other shapes up
+to the 64 KiB code limit (two K steps, the most tiles per wave), an all-zero input (the
+1e-12 amax clamp), and a NaN in x (NaN amax, NaN scale: every code of x is the NaN code)."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import gemm
+from oracle.linear import current_scaled_forward
+from tests.gpu_util import (assert_same_bytes, assert_within, dev_bf16, f32_bits, host_bf16_f64,
+                            host_u8, note)
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_fp8_linear_amd as m
+    m.load()
+    return m
+
+
+def _run(lib, x, w):
+    note(f"fp8_linear_fwd_current x {x.shape} w {w.shape}")
+    y, sc, qx, qw = lib.fp8_linear_fwd_current(dev_bf16(x), dev_bf16(w), want_codes=True)
+    torch.cuda.synchronize()
+    return host_bf16_f64(y), sc.cpu().numpy(), host_u8(qx), host_u8(qw)
+
+
+def _check(lib, x, w):
+    y, sc, qx, qw = _run(lib, x, w)
+    ref = current_scaled_forward(x, w)
+    want = [ref["sx"], ref["sw"], ref["sx_inv"], ref["sw_inv"]]
+    assert [f32_bits(v) for v in sc] == [f32_bits(v) for v in want], (sc, want)
+    assert_same_bytes(qx, ref["qx"], "qx")
+    assert_same_bytes(qw, ref["qw"], "qw")
+    D, tight = gemm.fp32_bound(ref["qx"], ref["qw"], ref["sx"], ref["sw"])
+    assert_within(y, D, gemm.error_bound(ref["qx"], ref["qw"], ref["sx"], ref["sw"]), "y")
+    assert_within(y, D, tight, "y (float32 accumulation)")
+
+
+def test_config1(lib):
+    d = workloads.linear_inputs(1)
+    assert d["x"].shape == (64, 128) and d["w"].shape == (128, 128)
+    _check(lib, d["x"], d["w"])
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (32, 96, 256), (256, 256, 128),
+                                   (128, 128, 256), (48, 208, 128)])
+def test_shapes(lib, M, N, K):
+    d = workloads.linear_inputs(2, 1, M=M, K=K, N=N)
+    _check(lib, d["x"], d["w"])
+    o = workloads.bf16_tensor("outlier_normal", (M, K), 5, 3 + M, 0, rate=0.01, mult=100.0)
+    _check(lib, o, d["w"])
+
+
+def test_zero_input(lib):
+    d = workloads.linear_inputs(1)
+    x = np.zeros_like(d["x"])
+    _check(lib, x, d["w"])
+
+
+def test_nan_in_x(lib):
+    d = workloads.linear_inputs(1)
+    x = d["x"].copy()
+    x[5, 17] = 0x7FC0                      # a quiet NaN
+    y, sc, qx, qw = _run(lib, x, d["w"])
+    ref = current_scaled_forward(x, d["w"])
+    assert np.isnan(sc[0]) and np.isnan(sc[2]) and np.isnan(ref["sx"])
+    assert f32_bits(sc[1]) == f32_bits(ref["sw"]) and f32_bits(sc[3]) == f32_bits(ref["sw_inv"])
+    assert_same_bytes(qx, ref["qx"], "qx (NaN multiplier)")
+    assert_same_bytes(qw, ref["qw"], "qw")
+    assert np.all(np.isnan(y))
