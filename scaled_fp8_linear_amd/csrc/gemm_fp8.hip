@@ -19,14 +19,18 @@
 // Kernels:
 //  * gemm_fp8_mx16_kernel (tensorwise, K of at least 512): 256x256 tiles, 4 waves of
 //    128x128 on v_mfma_f32_16x16x128_f8f6f4, 128-byte K stages in two LDS slots, one
-//    barrier per stage; described at the kernel;
-//  * gemm_fp8_mx16b_kernel (block recipe, K of at least 512): 256x128 tiles, 8 waves;
+//    barrier per stage, the epilogue split across the tile boundary; described at the
+//    kernel;
+//  * gemm_fp8_mx16bw_kernel (block recipe, K of at least 512, outputs of at least 256
+//    tiles): 256x256 tiles, 8 waves of 128x64 with the accumulators in VGPRs;
+//  * gemm_fp8_mx16b_kernel (block recipe, K of at least 512, other shapes): 256x128
+//    tiles, 8 waves of 64x64;
 //  * gemm_fp8_persist_kernel (small outputs and K): macro tile
 //    BM x BN, K advances 64 bytes per step (one v_mfma_f32_32x32x64_f8f6f4 per 32x32
 //    output tile and step), a ring of STAGES LDS arrays, one wait + barrier per step;
 //  * gemm_fp8_pipe_kernel: one tile per workgroup, for K step counts the persistent
 //    kernel's unrolled loop cannot divide.
-// Shared by all three:
+// Shared by all of them:
 //  * operand tiles go from memory straight into LDS with buffer loads that carry the
 //    "lds" modifier (no VGPR staging, no ds_write), issued through inline asm so the
 //    compiler does not add waits; the kernels wait (vmcnt) before the barrier that
@@ -42,7 +46,8 @@
 //    that run together share A and B panels in that XCD's L2;
 //  * epilogue: v_cvt_pk_bf16_f32 packs, a lane permute pairs results so that every
 //    lane stores 16 contiguous bytes through a buffer resource (pieces outside D are
-//    dropped by its range check); rows at or past M_valid are written as zeros.
+//    dropped by its range check); rows at or past M_valid are written as zeros (by the
+//    kernel, or for gemm_fp8_mx16_kernel by a fill kernel its launcher runs).
 #include <type_traits>
 
 #include "common.h"
