@@ -1427,11 +1427,16 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   // this stage's scales: fa[i] = sa of the lane's row in tile row i, times the wave's
   // weight scale when B has one per 128x128 block; with one per B row (BROWS = 1),
   // fb[4 j + r] = sb of the lane's column 4 g + r of tile column j
+  // PF (grouped scales, one weight scale per 128x128 block): a stage's scales are read in
+  // the previous stage's tail, after its barrier, into the other of two register sets, so
+  // that the stage's first folds do not wait for them
+  constexpr bool PF = SG && BROWS == 128;
   float fa[RT];
+  float fa2[PF ? RT : 1];
   float fb[BROWS == 1 ? 4 * CT : 1];
   const int pa = wm * WTM + r16 * (SG ? 1 : RT);   // the lane's first row-scale lane
   const int pb = BROWS == 1 ? BM + wn * WTN + 4 * g4 : BM + (wn * WTN) / 128;
-  auto rd_scales = [&](const uint8_t* sm, int rg, int q) {
+  auto rd_scales = [&](float* fs, const uint8_t* sm, int rg, int q) {
     static_assert(RT % 4 == 0, "row scales by 16 bytes");
     float fbw;
     if constexpr (SG) {
@@ -1442,7 +1447,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
       uint32_t ba = slot_addr(regions) + (uint32_t)(rg * kRegion) + 16u * pa + 4u * q;
       asm volatile("" : "+v"(ba));
 #pragma unroll
-      for (int i = 0; i < RT; ++i) fa[i] = *(lds_f32*)(uintptr_t)(ba + 256u * i);
+      for (int i = 0; i < RT; ++i) fs[i] = *(lds_f32*)(uintptr_t)(ba + 256u * i);
       uint32_t bb = slot_addr(regions) + (uint32_t)(rg * kRegion) + 16u * pb + 4u * q;
       asm volatile("" : "+v"(bb));
       if constexpr (BROWS == 1) {
@@ -1462,13 +1467,13 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
 #pragma unroll
       for (int v = 0; v < RT / 4; ++v) {
         const v4u a4 = lds16(ba + 16u * v);
-        fa[4 * v + 0] = __uint_as_float(a4.x); fa[4 * v + 1] = __uint_as_float(a4.y);
-        fa[4 * v + 2] = __uint_as_float(a4.z); fa[4 * v + 3] = __uint_as_float(a4.w);
+        fs[4 * v + 0] = __uint_as_float(a4.x); fs[4 * v + 1] = __uint_as_float(a4.y);
+        fs[4 * v + 2] = __uint_as_float(a4.z); fs[4 * v + 3] = __uint_as_float(a4.w);
       }
       fbw = *reinterpret_cast<const float*>(sm + kScaleOff + 4 * pb);
     }
 #pragma unroll
-    for (int i = 0; i < RT; ++i) fa[i] *= fbw;
+    for (int i = 0; i < RT; ++i) fs[i] *= fbw;
   };
 
   v4f acc[RT][CT];
@@ -1477,12 +1482,12 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
   Rows cur = rows_of(0), nxt = rows_of(1);
   int gq = 0;                                  // SG: scale groups begun before this tile
 
-  auto fold = [&](auto FIRST_, int x, const v4f& P) {
+  auto fold = [&](auto FIRST_, int x, const v4f& P, const float* fs) {
     constexpr bool FIRST = decltype(FIRST_)::value != 0;
     const int i = x / CT, j = x % CT;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float f = BROWS == 1 ? fa[i] * fb[4 * j + r] : fa[i];
+      const float f = BROWS == 1 ? fs[i] * fb[4 * j + r] : fs[i];
       acc[i][j][r] = FIRST ? P[r] * f : fmaf(P[r], f, acc[i][j][r]);
     }
   };
@@ -1499,7 +1504,8 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     v4f P[L + 1];
     const Bases qm = bases(mine);
     const int rg = (gq + s / kGroup) & 1;
-    rd_scales(mine, rg, Q);
+    float* const fs = (PF && Q % 2 == 1) ? fa2 : fa;     // this stage's scales
+    if constexpr (!PF) rd_scales(fa, mine, rg, Q);
     const int gs = s + 2;
     const Rows r = gs < ns ? cur : nxt;
     const int kb = gs < ns ? gs : gs - ns;
@@ -1513,7 +1519,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
       P[x % (L + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bq[j], Aq[i % kRing], z,
                                                                         0, 0, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (x >= L) fold(FIRST_, x - L, P[(x - L) % (L + 1)]);
+      if (x >= L) fold(FIRST_, x - L, P[(x - L) % (L + 1)], fs);
       // this stage's A rows, two ahead
       if (j == 0 && i + 2 < RT) Aq[(i + 2) % kRing] = rdA(qm, i + 2);
       if (x == kBarrierAt - 1) {
@@ -1531,6 +1537,9 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
         for (int d = y * kDma / kTail; d < (y + 1) * kDma / kTail; ++d) dma(d, mine, r, kb);
         if constexpr (SG && Q == 0)
           if (y == kTail - 1) dma_scales(rg ^ 1, r4, kb4);
+        // PF: the next stage's scales (the next group's region after Q = 3)
+        if constexpr (PF)
+          if (y == 1) rd_scales(Q % 2 == 1 ? fa : fa2, nullptr, Q == 3 ? rg ^ 1 : rg, (Q + 1) % 4);
         // the next stage's A rows 0 and 1, into the ring slots of rows RT - 4, RT - 3
         if (y == 0) Aq[0] = rdA(qo, 0);
         if (y == CT) Aq[1] = rdA(qo, 1);
@@ -1540,7 +1549,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int x = kMf - L; x < kMf; ++x) fold(FIRST_, x, P[x % (L + 1)]);
+    for (int x = kMf - L; x < kMf; ++x) fold(FIRST_, x, P[x % (L + 1)], fs);
   };
 
   auto epilogue = [&](int m0, int n0) {
@@ -1586,6 +1595,7 @@ gemm_fp8_mx16bw_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     for (int j = 0; j < CT; ++j) Bq[j] = rdB(q, j);
     Aq[0] = rdA(q, 0);
     Aq[1] = rdA(q, 1);
+    if constexpr (PF) rd_scales(fa, nullptr, 0, 0);   // stage 0 of the first tile
   }
   for (int ti = 0; ti < count; ++ti) {
     int cm0, cn0;
