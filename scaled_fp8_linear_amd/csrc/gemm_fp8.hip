@@ -727,11 +727,13 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // EPI = 1 (the LAST stage): after the first half, rows 0 .. RH-1 are final; their store
   //   ops run during the second half. All loads of that half (the next tile's stage 1) go
   //   out first, one per MFMA, and the ops (value and store) are spread over the MFMAs
-  //   left, so exactly kStores stores follow those loads.
-  // EPI = 2 (a FIRST stage after a tile): the first half's MFMAs write rows 0 .. RH-1 only,
-  //   so the previous tile's rows RH .. RT-1 (at em0, en0) go out in between. The wait in
-  //   the middle of the stage then lets those kStores stores stay in flight: loads and
-  //   stores retire in order, and the stage-1 loads it waits for were issued before them.
+  //   left.
+  // EPI = 2 (every tile's FIRST stage): the first half's MFMAs write rows 0 .. RH-1 only,
+  //   so the previous tile's rows RH .. RT-1 (at em0, en0) go out in between. With those of
+  //   EPI = 1, exactly kStores stores then follow the stage-1 loads, and the wait in the
+  //   middle of the stage lets them stay in flight: loads and stores retire in order, and
+  //   the loads it waits for were issued before them. Before the first tile there is no
+  //   previous tile (em0 = M): no stores, and the wait covers every load.
   auto stage = [&](auto FIRST_, auto LAST_, auto EPI_, int s, uint8_t* mine, uint8_t* other,
                    v8i* Bc, v8i* Bn, int em0, int en0) {
     constexpr bool FIRST = decltype(FIRST_)::value != 0, LAST = decltype(LAST_)::value != 0;
