@@ -98,12 +98,14 @@ def test_block_linear_step_wide_kernel(lib, M, K, N, rv):
 
 
 @pytest.mark.parametrize("M,K,N,rv", [(4224, 640, 4096, 4200), (4224, 4096, 640, 4200),
-                                      (4224, 512, 4096, 4224), (4224, 4096, 1536, 4100)])
+                                      (4224, 512, 4096, 4224), (4224, 4096, 1536, 4100),
+                                      (4224, 768, 4096, 4210)])
 def test_block_wide_tiles(lib, M, K, N, rv):
     """Outputs of at least 256 tiles of 256x256 take the 256x256-tile kernel (one weight scale
     per 128x128 block: forward, with y [M, N], and input gradient, with dx [M, K]): rows ragged
     against the tiles, padded token rows, an odd count of 128-wide blocks (5) in the
-    contraction, and counts divisible by 4 (4 and 12), whose scales load 4 blocks at a time
+    contraction, an even count not divisible by 4 (6: per-stage scale loads, no padding
+    stage), and counts divisible by 4 (4 and 12), whose scales load 4 blocks at a time
     into two alternating regions (one or three groups per tile, so the region of a tile's
     first group alternates between tiles). Every output against both bounds (the tolerance
     and float32 accumulation)."""
