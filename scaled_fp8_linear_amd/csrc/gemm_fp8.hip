@@ -114,6 +114,9 @@ __device__ __forceinline__ v4u lds16(uint32_t a) { return *(lds_v4u*)(uintptr_t)
 // stages with waits on it; the kernels wait for these loads themselves (vmcnt) before
 // the barrier that publishes a stage. Loads complete in order, which keeps every
 // compiler-inserted vmcnt wait for ordinary loads correct (at worst stricter).
+// The LDS address goes in M0, which the compiler treats as reserved (it warns that the
+// clobber may be ignored): no code generated for these kernels reads or writes M0 itself
+// (the LDS instructions of gfx950 do not use it), so only these loads set it.
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
@@ -1639,7 +1642,7 @@ __global__ void __launch_bounds__(C::kThreads, 1)
 gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                      const float* __restrict__ sa, const float* __restrict__ sb,
                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ D, int M, int N,
-                     int K, int M_valid, int tiles_m, int tiles_n) {
+                     int K, int M_valid, int tiles_n) {
   static_assert(!C::BLOCK, "tensorwise only");
   constexpr int SB = C::kStageBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t s0[SB];
@@ -1707,7 +1710,7 @@ hipError_t run_pipe(const uint8_t* A, const uint8_t* B, const float* sa, const f
   const int tiles_n = (N + C::BN - 1) / C::BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   hipLaunchKernelGGL(gemm_fp8_pipe_kernel<C>, dim3((unsigned)tiles), dim3(C::kThreads), 0, s, A,
-                     B, sa, sb, bias, D, M, N, K, M_valid, tiles_m, tiles_n);
+                     B, sa, sb, bias, D, M, N, K, M_valid, tiles_n);
   return hipGetLastError();
 }
 
