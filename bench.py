@@ -52,6 +52,10 @@ def _parse():
     ap.add_argument("--profile-gemms", action="store_true",
                     help="only run every GEMM launch shape of the step and of the block recipe "
                          "(5 launches each after 2 warm-up launches), for counter collection")
+    ap.add_argument("--compare-hipblaslt", action="store_true",
+                    help="only run each tensorwise GEMM launch shape of the step with this "
+                         "library and with torch._scaled_mm (hipBLASLt) on the same codes: "
+                         "bytes compared, 40 launches of each, for a kernel trace")
     return ap.parse_args()
 
 
@@ -168,6 +172,60 @@ def profile_gemms(launches=5, warmup=2):
           lambda: m.fp8_linear_dgrad(qg, qw_t, sg, sw_t, dx=dx, gran=B), f)
     timed("block wgrad 8192x8192x16384",
           lambda: m.fp8_linear_wgrad(qg_t, qx_t, sg_t, sx_t, dw=dw, gran=B), f)
+
+
+def compare_hipblaslt(blocks=4, per_block=10, warmup=3):
+    """The step's four tensorwise GEMM launch shapes, each run with this library and with
+    torch._scaled_mm (hipBLASLt's FP8 GEMM) on the same operand codes (quantized by the library
+    from N(0, 1) and N(0, 0.02) data with the scales their amaxes give), in alternating blocks
+    of launches so that neither meets a different clock. Prints, per shape, how many output
+    elements differ in their bytes and the mean event time per launch of each; meant to run
+    under a kernel trace as well."""
+    import torch
+    import scaled_fp8_linear_amd as m
+    m.load()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(5)
+
+    def block_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(per_block):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / per_block
+
+    for M, N, K in ((8192, 14336, 4096), (8192, 4096, 14336), (14336, 4096, 8192),
+                    (4096, 14336, 8192)):
+        xa = torch.randn(M, K, device=dev, generator=gen).to(torch.bfloat16)
+        xb = (torch.randn(N, K, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+        amax_a, amax_b = xa.abs().max().float(), xb.abs().max().float()
+        sa, sb = (amax_a / 448).reshape(1), (amax_b / 448).reshape(1)
+        qa = m.fp8_quantize_amax(xa, scale_inv=(448 / amax_a).reshape(1), want_q_t=False)[0]
+        qb = m.fp8_quantize_amax(xb, scale_inv=(448 / amax_b).reshape(1), want_q_t=False)[0]
+        del xa, xb
+        fa, fb = qa.view(torch.float8_e4m3fn), qb.view(torch.float8_e4m3fn)
+        y = m.fp8_linear_fwd(qa, qb, sa, sb)
+        r = torch._scaled_mm(fa, fb.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        differ = int((y.view(torch.int16) != r.view(torch.int16)).sum())
+        run = {"fp8lin": lambda: m.fp8_linear_fwd(qa, qb, sa, sb, y=y),
+               "hipblaslt": lambda: torch._scaled_mm(fa, fb.t(), scale_a=sa, scale_b=sb,
+                                                     out_dtype=torch.bfloat16)}
+        for fn in run.values():
+            for _ in range(warmup):
+                fn()
+        us = {k: 0.0 for k in run}
+        for b in range(blocks):
+            for k in (("fp8lin", "hipblaslt") if b % 2 == 0 else ("hipblaslt", "fp8lin")):
+                us[k] += block_us(run[k]) / blocks
+        ours, theirs = us["fp8lin"], us["hipblaslt"]
+        print(json.dumps({"shape": [M, N, K], "elements": M * N, "elements_differing": differ,
+                          "fp8lin_us": round(ours, 1), "hipblaslt_us": round(theirs, 1)}),
+              flush=True)
+        del qa, qb, fa, fb, y, r
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mlp_8192x4096x14336.txt")
@@ -824,6 +882,9 @@ def main():
         return
     if args.profile_gemms:
         profile_gemms()
+        return
+    if args.compare_hipblaslt:
+        compare_hipblaslt()
         return
 
     import torch
