@@ -521,9 +521,10 @@ constexpr int kStageK = 128;   // K bytes per LDS stage of gemm_fp8_mx16_kernel
 //   first half  (rows 0 .. RT/2-1): A fragments of rows 1 .. RT-1 are read in between;
 //   mid-stage:  the wave waits for its loads of stage s + 1; a barrier publishes them
 //               and frees this stage's slot (all its reads are done by then);
-//   second half (the other rows): the loads of stage s + 2 go into this slot, and stage
-//               s + 1's B fragments and A row 0 are read.
-// B fragments of a stage stay in registers for all its MFMAs (two sets alternate).
+//   second half (the other rows, tile column by tile column): the loads of stage s + 2
+//               go into this slot, and stage s + 1's A row 0 is read, and its B fragment
+//               j right after this stage's last MFMA with B fragment j (one set of B
+//               registers).
 // Fragment of a 16-row tile: lane l holds 32 bytes of row l % 16 at K offset
 // 32 (l / 16); the instruction pairs A and B by lane and byte, so this K order is as
 // good as any. The B tile goes in as the first operand, so a lane's 4 results are 4
@@ -549,6 +550,10 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
                 C::BN % (kRowsPerInst * C::kWaves) == 0, "load instructions");
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[SB];
+  // STAGED (wave tiles 128 outputs wide, no bias): the output passes through 4 KB of LDS
+  // per wave so that every store writes whole 128-byte lines (see op_emit)
+  constexpr bool kStaged = C::WTN == 128 && !BIAS;
+  __shared__ __attribute__((aligned(1024))) uint8_t stg_mem[kStaged ? 4096 * C::kWaves : 16];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -640,10 +645,11 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   };
 
   v4f acc[RT][CT];
-  // B fragments of this stage and the next (two sets alternate); A rows 0 .. RH-1 and
-  // RH .. RT-1 of this stage. Only B and A row 0 are read a stage ahead: rows 1 .. RT-1
-  // are read during the stage's first half, which keeps the register peak down.
-  v8i Bf0[CT], Bf1[CT], Alo[RH], Ahi[RS];
+  // B fragments (one set: fragment j of stage s + 1 replaces stage s's after its last
+  // MFMA); A rows 0 .. RH-1 and RH .. RT-1 of this stage. Only B and A row 0 are read a
+  // stage ahead: rows 1 .. RT-1 are read during the stage's first half, which keeps the
+  // register peak down.
+  v8i Bf[CT], Alo[RH], Ahi[RS];
 
   // stages per tile: K / 128 rounded up to an even count of at least 4; stages past K
   // (the tail of a K that is not a multiple of 256) load zeros
@@ -658,6 +664,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // only) and are dropped there; the launcher writes their zeros.
   constexpr int kPairs = CT / 2, kOps = kPairs + CT % 2;   // store ops per row
   static_assert(kStores == RT * kOps, "store count");
+  static_assert(!kStaged || kOps == 4, "a staged row is 4 ops: 2 chunk columns of 2 pairs");
   typedef int v2i __attribute__((ext_vector_type(2)));
   // BIAS: tile j's 4 columns of the lane are n0 + wn WTN + 16 j + 4 g .. + 3 (packed bf16;
   // columns past N read as 0)
@@ -721,8 +728,70 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     }
   };
 
-  // One stage. Bc and Alo[0]: this stage's B fragments and A row 0 (read before); Bn and
-  // Alo[0]: the next stage's, read in the second half.
+  // STAGED. An op's 16 bytes per lane are 8 outputs of ITS row (l % 16), 4 lanes per row, so
+  // a direct store writes 16 rows of 64 bytes: half lines, which cost the memory pipeline
+  // about as many cycles as whole ones. Staged, op o of row i writes its piece into the
+  // wave's 16 staging rows of 256 bytes (row r16, 16-byte chunk c = 4 o + 2 (g % 2) + g / 2,
+  // the piece's 8 columns / 8); a row's chunk c (h = c % 2: rows 8 h .. 8 h + 7; q = c / 2:
+  // columns 64 q .. 64 q + 63, complete once pairs 2 q and 2 q + 1 are written) is read back
+  // so that lane l holds row 8 h + l / 8, columns 64 q + 8 (l % 8), and stored: 8 rows of
+  // 128 bytes. Op k of a half reads and stores the chunk two ops behind it (row i's chunk
+  // o - 2, or the row before's chunk o + 2) before it computes its own piece, which hides
+  // the read's latency; the half's last op also stores its row's chunks 2 and 3. Pairs 0
+  // and 1 of a row overwrite chunks 0 to 7 of the staging rows only after the row before's
+  // chunks 2 and 3 (16-byte chunks 8 to 15) were read. Each row still takes kOps stores, so
+  // the waits that count stores in flight stay exact. A wave reads only what it wrote and
+  // its LDS operations complete in order: no barrier. 16-byte chunk c of staging row r
+  // sits at c ^ sw(r), sw(r) = (r & 1) | (r & 2) << 2 | (r & 8) >> 1, which spreads both the
+  // writes and the whole-line reads over the banks, for the 16-lane groups gfx950 serves a
+  // 16-byte LDS access in.
+  auto stg_sw = [](int r) { return (r & 1) | ((r & 2) << 2) | ((r & 8) >> 1); };
+  const uint32_t stg = lds_addr(stg_mem) + 4096u * (uint32_t)wave;
+  // the lane's staging addresses for op 0 (write) and for chunk 0 (read); an op or chunk
+  // flips chunk bits only (XOR inside the 256-byte row), since sw(8 h + r) = sw(r) ^ 4 h
+  const uint32_t stg_w =
+      stg + 256u * (uint32_t)r16 + 16u * (uint32_t)((2 * (g4 & 1) + (g4 >> 1)) ^ stg_sw(r16));
+  const uint32_t stg_r =
+      stg + 256u * (uint32_t)(lane >> 3) + 16u * (uint32_t)((lane & 7) ^ stg_sw(lane >> 3));
+  const int fcol = wn * C::WTN + 8 * (lane & 7);
+  const uint32_t frow_off =
+      (uint32_t)(wm * C::WTM + (lane >> 3)) * (uint32_t)N * 2u + 2u * (uint32_t)fcol;
+  typedef __attribute__((address_space(3))) v4i lds_v4i;
+  // op k of a half that starts at row i0 and has kn ops
+  auto op_emit = [&](int k, int i0, int kn, int m0, int n0) {
+    const int i = i0 + k / kOps, o = k % kOps;
+    if constexpr (!kStaged) {
+      op_store(i, o, op_value(i, o), m0, n0);
+    } else {
+      auto chunk_read = [&](int c) {
+        const int h = c & 1, q = c >> 1;
+        return *(lds_v4i*)(uintptr_t)((stg_r ^ (128u * q + 64u * h)) + 2048u * h);
+      };
+      auto chunk_store = [&](v4i w, int row, int c) {
+        const int h = c & 1, q = c >> 1;
+        const uint32_t base = ((uint32_t)(m0 + 16 * row) * (uint32_t)N + (uint32_t)n0) * 2u;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            w, rsD,
+            fcol + 64 * q < N - n0 ? base + frow_off + 16u * (uint32_t)N * h + 128u * q
+                                   : kOutOfRange,
+            0, 0);
+      };
+      const bool behind = k >= 2;
+      const int prow = o >= 2 ? i : i - 1, pc = o >= 2 ? o - 2 : o + 2;
+      v4i w;
+      if (behind) w = chunk_read(pc);
+      *(lds_v4i*)(uintptr_t)(stg_w ^ (64u * (uint32_t)o)) = op_value(i, o);
+      if (behind) chunk_store(w, prow, pc);
+      if (k == kn - 1) {
+        chunk_store(chunk_read(2), i, 2);
+        chunk_store(chunk_read(3), i, 3);
+      }
+    }
+  };
+
+  // One stage. Bf and Alo[0]: this stage's B fragments and A row 0 (read before); the
+  // next stage's are read in the second half, B fragment j into Bf[j] right after this
+  // stage's last MFMA with it (the second half runs tile column by tile column).
   // FIRST: the tile's first stage (sums start at zero). LAST: the tile's last stage, which
   // reads no fragments of the next stage (they are read after it, so that they hold no
   // registers through it).
@@ -738,7 +807,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   //   the loads it waits for were issued before them. Before the first tile there is no
   //   previous tile (em0 = M): no stores, and the wait covers every load.
   auto stage = [&](auto FIRST_, auto LAST_, auto EPI_, int s, uint8_t* mine, uint8_t* other,
-                   v8i* Bc, v8i* Bn, int em0, int en0) {
+                   int em0, int en0) {
     constexpr bool FIRST = decltype(FIRST_)::value != 0, LAST = decltype(LAST_)::value != 0;
     constexpr int EPI = decltype(EPI_)::value;
     static_assert(EPI != 1 || LAST, "the first epilogue half runs in a last stage");
@@ -757,13 +826,13 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 #pragma unroll
       for (int x = 0; x < kMf; ++x) {
         const int i = x / CT, j = x % CT;
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Alo[i], z, 0,
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bf[j], Alo[i], z, 0,
                                                                      C::AFMT, 0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (em0 < M) {             // false before the first tile: nothing to store
 #pragma unroll
           for (int k = x * kEp / kMf; k < (x + 1) * kEp / kMf; ++k)
-            op_store(RH + k / kOps, k % kOps, op_value(RH + k / kOps, k % kOps), em0, en0);
+            op_emit(k, RH, kEp, em0, en0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -772,7 +841,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
       for (int i = 0; i < RH; ++i)
 #pragma unroll
         for (int j = 0; j < CT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Alo[i],
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bf[j], Alo[i],
                                                                        FIRST ? z : acc[i][j], 0,
                                                                        C::AFMT, 0, 0, 0, 0);
 #pragma unroll
@@ -803,8 +872,8 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     static_assert(EPI != 1 || kDma < kSecond, "the loads go out before the stores");
 #pragma unroll
     for (int x = 0; x < kSecond; ++x) {
-      const int i = RH + x / CT, j = x % CT;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bc[j], Ahi[i - RH],
+      const int i = RH + x % RS, j = x / RS;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Bf[j], Ahi[i - RH],
                                                                    FIRST ? z : acc[i][j], 0,
                                                                    C::AFMT, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -814,17 +883,15 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 #pragma unroll
         for (int k = 0; k < kEpLo; ++k)
           if (kDma + k * (kSecond - kDma) / kEpLo == x)
-            op_store(k / kOps, k % kOps, op_value(k / kOps, k % kOps), em0, en0);
+            op_emit(k, 0, kEpLo, em0, en0);
       } else {
         if (x * kDma / kSecond != (x + 1) * kDma / kSecond) dma(x * kDma / kSecond, mine, r, kb);
-        // the next stage's B fragments over the first kSecond - kLeadA MFMAs, then its A
-        // row 0, kLeadA MFMAs before the stage ends (late enough to take the registers of
-        // B fragments this half is done with, early enough that the next stage's first MFMA
-        // does not wait for it)
+        // the next stage's B fragment j after this stage's last MFMA with it (CT - 1 MFMAs
+        // or more before the next stage's first use of it), and its A row 0 kLeadA MFMAs
+        // before the stage ends (early enough that the next stage's first MFMA does not
+        // wait for it)
         if constexpr (!LAST) {
-#pragma unroll
-          for (int f = 0; f < CT; ++f)
-            if (f * (kSecond - kLeadA) / CT == x) Bn[f] = rdB(other, f);
+          if (x % RS == RS - 1) Bf[j] = rdB(other, j);
           if (x == kSecond - kLeadA) Alo[0] = rdA(other, 0);
         }
       }
@@ -842,7 +909,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // stage 0 of a tile: its B fragments and A rows 0 .. RH-1 (slot 0, published)
   auto first_frags = [&]() {
 #pragma unroll
-    for (int j = 0; j < CT; ++j) Bf0[j] = rdB(slot0, j);
+    for (int j = 0; j < CT; ++j) Bf[j] = rdB(slot0, j);
     Alo[0] = rdA(slot0, 0);
   };
   first_frags();
@@ -852,14 +919,14 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     int cm0, cn0;
     tile_mn(ti, cm0, cn0);
     // stages 0, 1 | 2 .. ns - 3 | ns - 2, ns - 1 (ns is even and at least 4)
-    stage(IC<1>{}, IC<0>{}, IC<2>{}, 0, slot0, slot1, Bf0, Bf1, pm0, pn0);
-    stage(IC<0>{}, IC<0>{}, IC<0>{}, 1, slot1, slot0, Bf1, Bf0, 0, 0);
+    stage(IC<1>{}, IC<0>{}, IC<2>{}, 0, slot0, slot1, pm0, pn0);
+    stage(IC<0>{}, IC<0>{}, IC<0>{}, 1, slot1, slot0, 0, 0);
     for (int s = 2; s < ns - 2; s += 2) {
-      stage(IC<0>{}, IC<0>{}, IC<0>{}, s, slot0, slot1, Bf0, Bf1, 0, 0);
-      stage(IC<0>{}, IC<0>{}, IC<0>{}, s + 1, slot1, slot0, Bf1, Bf0, 0, 0);
+      stage(IC<0>{}, IC<0>{}, IC<0>{}, s, slot0, slot1, 0, 0);
+      stage(IC<0>{}, IC<0>{}, IC<0>{}, s + 1, slot1, slot0, 0, 0);
     }
-    stage(IC<0>{}, IC<0>{}, IC<0>{}, ns - 2, slot0, slot1, Bf0, Bf1, 0, 0);
-    stage(IC<0>{}, IC<1>{}, IC<1>{}, ns - 1, slot1, slot0, Bf1, Bf0, cm0, cn0);
+    stage(IC<0>{}, IC<0>{}, IC<0>{}, ns - 2, slot0, slot1, 0, 0);
+    stage(IC<0>{}, IC<1>{}, IC<1>{}, ns - 1, slot1, slot0, cm0, cn0);
     first_frags();                     // the next tile's stage 0, published at stage ns - 1
     pm0 = cm0;
     pn0 = cn0;
@@ -870,7 +937,7 @@ gemm_fp8_mx16_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     // the last tile's rows RH .. RT-1
 #pragma unroll
     for (int k = 0; k < RS * kOps; ++k)
-      op_store(RH + k / kOps, k % kOps, op_value(RH + k / kOps, k % kOps), pm0, pn0);
+      op_emit(k, RH, RS * kOps, pm0, pn0);
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // no load may land after exit
 }
