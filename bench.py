@@ -432,7 +432,7 @@ def measure_config1(torch, m, workloads, iters=200, repeats=7):
                                 want_amax=False)
         m.fp8_linear_fwd(q["x"], q["w"], sc["x"], sc["w"], y=y)
 
-    def per_call_us(fn):
+    def per_call_us(fn, iters=iters):
         for _ in range(20):
             fn()
         out = []
@@ -462,7 +462,7 @@ def measure_config1(torch, m, workloads, iters=200, repeats=7):
     torch.cuda.synchronize()
     same = bool(torch.equal(y.view(torch.int16), ref.view(torch.int16)))
     graph_us = per_call_us(graph.replay)
-    # the same forward as one launch (amaxes, scales, casts and GEMM in one workgroup)
+    # the same forward as one launch (amaxes, scales, casts and GEMM, one workgroup per tile)
     y1 = torch.empty((64, 128), dtype=torch.bfloat16, device=dev)
     sc1 = torch.empty(4, **f32)
     q1 = {"x": torch.empty((64, 128), dtype=torch.uint8, device=dev),
@@ -483,6 +483,14 @@ def measure_config1(torch, m, workloads, iters=200, repeats=7):
     with torch.cuda.graph(gf):
         fused()
     fused_graph_us = per_call_us(gf.replay)
+    # GPU time per forward: one graph of back-to-back forwards, so neither the host nor a
+    # replay's own start is in the figure
+    chain = 32
+    gc = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gc):
+        for _ in range(chain):
+            fused()
+    chain_us = per_call_us(gc.replay, iters=20) / chain
     flops = 2.0 * 64 * 128 * 128
     return {"workload": "one fp8 linear forward, current tensorwise scaling, x [64,128], "
                         "W [128,128] N(0,1): amax pass, scale, cast for x and W, then the GEMM",
@@ -493,6 +501,8 @@ def measure_config1(torch, m, workloads, iters=200, repeats=7):
             "one_launch": {"entry": "fp8_linear_fwd_current",
                            "us_per_forward_eager": round(fused_us, 2),
                            "us_per_forward_hip_graph": round(fused_graph_us, 2),
+                           "us_per_forward_gpu": round(chain_us, 2),
+                           "gpu_time_of": f"one HIP graph of {chain} forwards back to back",
                            "codes_and_scales_match_seven_launches": fused_same,
                            "gflops_hip_graph": round(flops / (fused_graph_us * 1e-6) / 1e9, 2)}}
 

@@ -255,8 +255,9 @@ int fp8_linear_wgrad(const void* qg_t, const void* qx_t, const float* sg, const 
  * launch).
  *
  *   x       bf16 [M, K]; w bf16 [N, K]. M, N positive multiples of 16, K a
- *           positive multiple of 128, and (M + N) * K <= 65536 (the operands'
- *           codes fit one workgroup's LDS); larger linears use fp8_quantize_amax,
+ *           positive multiple of 128, and (M + N) * K <= 65536: one workgroup per
+ *           16x16 tile of y reads the whole of both operands for the amaxes, so
+ *           this call is for small linears only; larger ones use fp8_quantize_amax,
  *           fp8_scale_update and fp8_linear_fwd (FP8_ERR_UNSUPPORTED says so).
  *   y       bf16 [M, N] out: y[m,n] = bf16_rne(float32(sx * sw) *
  *           sum_k qx[m,k] * qw[n,k]), float32 accumulation.

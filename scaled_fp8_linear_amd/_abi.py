@@ -91,7 +91,8 @@ def _ptr(t, offset_elems: int = 0):
         raise ValueError("fp8lin takes device tensors")
     if not t.is_contiguous():
         raise ValueError("fp8lin takes contiguous row-major tensors")
-    return t.data_ptr() + offset_elems * t.element_size()
+    p = t.data_ptr()
+    return p + offset_elems * t.element_size() if offset_elems else p
 
 
 def _stream(stream):
@@ -154,14 +155,17 @@ def _need(t, name, shape, dtypes, dev=None):
     ValueError; nothing has been enqueued at that point."""
     if t is None:
         return
+    # one combined test on the common path (every attribute read costs), the reason after
+    if (t.dtype in dtypes and t.shape == tuple(shape) and t.is_contiguous()
+            and (dev is None or t.device == dev)):
+        return
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if tuple(t.shape) != tuple(int(v) for v in shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous (row-major)")
-    if dev is not None and t.device != dev:
-        raise ValueError(f"{name} is on {t.device}, the operands on {dev}")
+    raise ValueError(f"{name} is on {t.device}, the operands on {dev}")
 
 
 def _need_scalar(v, name, dev=None, count=1):

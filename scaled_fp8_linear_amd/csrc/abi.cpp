@@ -197,7 +197,7 @@ int fp8_linear_fwd_current(const void* x, const void* w, int64_t M, int64_t N, i
                 fn, (long long)M, (long long)N, (long long)K);
   if ((M + N) * K > fp8lin::kSmallLinearCodes)
     return fail(FP8_ERR_UNSUPPORTED,
-                "%s: (M + N) K = %lld bytes of codes exceed the one-workgroup limit of %d; use "
+                "%s: (M + N) K = %lld bytes of codes exceed the small-linear limit of %d; use "
                 "fp8_quantize_amax, fp8_scale_update and fp8_linear_fwd",
                 fn, (long long)((M + N) * K), fp8lin::kSmallLinearCodes);
   if (!x || !w || !y || !scales) return fail(FP8_ERR_NULL, "%s: NULL x, w, y or scales", fn);

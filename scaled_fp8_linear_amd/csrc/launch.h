@@ -30,8 +30,10 @@ hipError_t launch_scale_update(int mode, float* amax, bool clear_amax, float* hi
                                int32_t pos, float* scale, float* scale_inv, bool e5m2,
                                hipStream_t s);
 
-// Current-scaling forward of a small linear in one workgroup: the operands' codes,
-// (M + N) K bytes, live in LDS between the cast and the GEMM.
+// Current-scaling forward of a small linear in one launch, one workgroup per 16x16 tile of
+// y. Each workgroup reads the whole of x and W for the amaxes, so (M + N) K, the bytes of
+// codes of both operands, is capped; a tile's own 32 K bytes of codes live in LDS between
+// the cast and the GEMM.
 constexpr int kSmallLinearCodes = 64 * 1024;
 hipError_t launch_linear_current_small(const uint16_t* x, const uint16_t* w, int M, int N, int K,
                                        uint16_t* y, float* scales, uint8_t* qx, uint8_t* qw,

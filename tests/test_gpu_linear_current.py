@@ -1,16 +1,18 @@
 """The one-launch current-scaling forward of a small linear (fp8_linear_fwd_current)
 against the oracle: amaxes, scales and multipliers bit for bit, the codes byte for byte,
 y within both GEMM bounds. Config 1 (x [64, 128], W [128, 128], N(0, 1)), other shapes up
-to the 64 KiB code limit (two K steps, the most tiles per wave), an all-zero input (the
-1e-12 amax clamp), and a NaN in x (NaN amax, NaN scale: every code of x is the NaN code)."""
+to the 64 KiB code limit (one 16x16 tile per workgroup: up to 256 tiles, up to 16 K steps;
+amax loads all at once or in batches; a tile's own rows held from the start or read again),
+the codes not asked for, an all-zero input (the 1e-12 amax clamp), and a NaN in x (NaN
+amax, NaN scale: every code of x is the NaN code)."""
 import numpy as np
 import pytest
 
 import workloads
 from oracle import gemm
 from oracle.linear import current_scaled_forward
-from tests.gpu_util import (assert_same_bytes, assert_within, dev_bf16, f32_bits, host_bf16_f64,
-                            host_u8, note)
+from tests.gpu_util import (assert_same_bytes, assert_within, dev_bf16, f32_bits, host_bf16_bits,
+                            host_bf16_f64, host_u8, note)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -51,12 +53,26 @@ def test_config1(lib):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (32, 96, 256), (256, 256, 128),
-                                   (128, 128, 256), (48, 208, 128)])
+                                   (128, 128, 256), (48, 208, 128), (16, 496, 128),
+                                   (112, 16, 128), (32, 16, 512), (16, 16, 2048)])
 def test_shapes(lib, M, N, K):
     d = workloads.linear_inputs(2, 1, M=M, K=K, N=N)
     _check(lib, d["x"], d["w"])
     o = workloads.bf16_tensor("outlier_normal", (M, K), 5, 3 + M, 0, rate=0.01, mult=100.0)
     _check(lib, o, d["w"])
+
+
+def test_codes_not_wanted(lib):
+    d = workloads.linear_inputs(2, 1, M=48, K=384, N=80)
+    _check(lib, d["x"], d["w"])
+    note("fp8_linear_fwd_current x (48, 384) w (80, 384), with and without qx, qw")
+    y1, sc1, _, _ = lib.fp8_linear_fwd_current(dev_bf16(d["x"]), dev_bf16(d["w"]),
+                                               want_codes=True)
+    y2, sc2, qx2, qw2 = lib.fp8_linear_fwd_current(dev_bf16(d["x"]), dev_bf16(d["w"]))
+    torch.cuda.synchronize()
+    assert qx2 is None and qw2 is None
+    assert_same_bytes(host_bf16_bits(y2), host_bf16_bits(y1), "y")
+    assert_same_bytes(host_u8(sc2), host_u8(sc1), "scales")
 
 
 def test_zero_input(lib):
