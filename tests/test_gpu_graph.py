@@ -98,3 +98,21 @@ def test_config1_forward_graph_replays(lib):
                                                want_q_t=False)
         lib.fp8_linear_fwd(qo, qo, torch.ones(1, **f32), torch.ones(1, **f32))
         torch.cuda.synchronize()
+
+
+def test_calls_without_a_stream_use_torch_current_stream(lib):
+    """A call given no stream is enqueued on torch's current stream: the default stream, a side
+    stream made current (checked here), and the capture stream (the replays above)."""
+    from scaled_fp8_linear_amd import _abi
+    note("binding stream resolution")
+    assert _abi._stream(None) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert _abi._stream(None) == side.cuda_stream
+        d = workloads.linear_inputs(1)
+        y, sc, _, _ = lib.fp8_linear_fwd_current(dev_bf16(d["x"]), dev_bf16(d["w"]))
+    torch.cuda.current_stream().wait_stream(side)
+    assert _abi._stream(None) == torch.cuda.current_stream().cuda_stream
+    y2, sc2, _, _ = lib.fp8_linear_fwd_current(dev_bf16(d["x"]), dev_bf16(d["w"]))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)) and torch.equal(sc, sc2)
