@@ -3,8 +3,8 @@ against the oracle: amaxes, scales and multipliers bit for bit, the codes byte f
 y within both GEMM bounds. Config 1 (x [64, 128], W [128, 128], N(0, 1)), other shapes up
 to the 64 KiB code limit (one 16x16 tile per workgroup: up to 256 tiles, up to 16 K steps;
 amax loads all at once or in batches; a tile's own rows held from the start or read again),
-the codes not asked for, an all-zero input (the 1e-12 amax clamp), and a NaN in x (NaN
-amax, NaN scale: every code of x is the NaN code)."""
+the codes not asked for or only one of them, an all-zero input (the 1e-12 amax clamp), and a
+NaN in x or in W (NaN amax, NaN scale: every code of that operand is the NaN code)."""
 import numpy as np
 import pytest
 
@@ -91,4 +91,31 @@ def test_nan_in_x(lib):
     assert f32_bits(sc[1]) == f32_bits(ref["sw"]) and f32_bits(sc[3]) == f32_bits(ref["sw_inv"])
     assert_same_bytes(qx, ref["qx"], "qx (NaN multiplier)")
     assert_same_bytes(qw, ref["qw"], "qw")
+    assert np.all(np.isnan(y))
+
+
+def test_one_code_tensor(lib):
+    """qx asked for without qw, then qw without qx: each is written whole by its own tiles."""
+    d = workloads.linear_inputs(2, 1, M=48, K=256, N=64)
+    ref = current_scaled_forward(d["x"], d["w"])
+    note("fp8_linear_fwd_current x (48, 256) w (64, 256), qx only then qw only")
+    qx = torch.full((48, 256), 0xAB, dtype=torch.uint8, device="cuda")
+    lib.fp8_linear_fwd_current(dev_bf16(d["x"]), dev_bf16(d["w"]), qx=qx)
+    qw = torch.full((64, 256), 0xAB, dtype=torch.uint8, device="cuda")
+    lib.fp8_linear_fwd_current(dev_bf16(d["x"]), dev_bf16(d["w"]), qw=qw)
+    torch.cuda.synchronize()
+    assert_same_bytes(host_u8(qx), ref["qx"], "qx")
+    assert_same_bytes(host_u8(qw), ref["qw"], "qw")
+
+
+def test_nan_in_w(lib):
+    d = workloads.linear_inputs(2, 1, M=32, K=128, N=48)
+    w = d["w"].copy()
+    w[40, 3] = 0xFFC0                      # a negative quiet NaN, in the last tile row of W
+    y, sc, qx, qw = _run(lib, d["x"], w)
+    ref = current_scaled_forward(d["x"], w)
+    assert np.isnan(sc[1]) and np.isnan(sc[3]) and np.isnan(ref["sw"])
+    assert f32_bits(sc[0]) == f32_bits(ref["sx"]) and f32_bits(sc[2]) == f32_bits(ref["sx_inv"])
+    assert_same_bytes(qx, ref["qx"], "qx")
+    assert_same_bytes(qw, ref["qw"], "qw (NaN multiplier)")
     assert np.all(np.isnan(y))
